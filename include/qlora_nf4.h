@@ -1,0 +1,181 @@
+/*
+ * qlora_nf4.h -- C ABI of the MI355X (gfx950) NF4 dequant-GEMM library.
+ *
+ * The library implements the data-parallel hot path of QLoRA as the pages
+ * describe it:
+ *   - block-wise 4-bit NormalFloat (NF4) quantization of a frozen weight,
+ *     one 32-bit absmax constant per block of 64 weights
+ *     ("A 65B fine-tune on the GPU you already have", figures 3 and 4;
+ *      "QLoRA and Quantized Training", section "The idea");
+ *   - double quantization of those constants to 8 bits in groups of 256
+ *     blocks (same page, figure 4);
+ *   - the matmul through the frozen base with the weights dequantized to
+ *     bf16 block by block right before the multiply, plus the LoRA adapter
+ *     term, forward and backward-to-input
+ *     (same page, figure 2; "QLoRA Explained: 4-bit NF4, ...", section
+ *      "What is QLoRA?"; "QLoRA and Quantized Training", section "In code").
+ *
+ * Storage format produced and consumed here (for a weight W of numel values,
+ * nb = numel / 64 blocks, ng = ceil(nb / 256) groups):
+ *   packed  uint8[numel/2]  two 4-bit codes per byte, element 2i in the low
+ *                           nibble of byte i; code = index of the nearest of
+ *                           the 16 levels, ties to the lower index
+ *   absmax  float[nb]       per-block max |w| (the first-level constant)
+ *   qscale  int8[nb]        q_b = rne(absmax_b / d_g), clamped to +-127
+ *   step    float[ng]       d_g = max(absmax over group g) / 127
+ * Dequantized weight: w' = bf16_rne(L[code] * fp32(q_b * d_g)).
+ * The 16 levels L are the quantiles of N(0,1) at probabilities (i+1/2)/16,
+ * divided by the largest one (so L[0] = -1, L[15] = +1).
+ *
+ * Conventions for every entry point:
+ *   - bf16 tensors are passed as uint16_t bit patterns; all matrices are
+ *     row-major and densely packed (leading dimension = number of columns).
+ *   - Every pointer argument except those of qlora_nf4_codebook is a DEVICE
+ *     pointer owned by the caller. The library never allocates or frees
+ *     device memory and keeps no per-call state; it is safe to call from
+ *     several threads.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Calls enqueue
+ *     their kernels on it and return without synchronising; outputs are
+ *     valid once the stream has reached them, and every buffer must stay
+ *     alive until then.
+ *   - Arguments are validated before anything is launched. A failed check
+ *     returns a non-zero qlora_status and launches nothing. Nothing is
+ *     printed and nothing aborts. A HIP launch failure returns
+ *     QLORA_ERR_HIP; qlora_last_hip_error() gives the hipError_t.
+ *   - Weights must be finite; NaN/Inf inputs give unspecified codes.
+ */
+#ifndef QLORA_NF4_H
+#define QLORA_NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QLORA_OK = 0,
+  QLORA_ERR_NULL = 1,      /* a required pointer is NULL */
+  QLORA_ERR_SHAPE = 2,     /* a size is out of range or not a multiple it must be */
+  QLORA_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned */
+  QLORA_ERR_RANK = 4,      /* LoRA rank out of range or adapters inconsistent */
+  QLORA_ERR_WORKSPACE = 5, /* workspace missing or smaller than required */
+  QLORA_ERR_DTYPE = 6,     /* unknown input dtype */
+  QLORA_ERR_HIP = 7,       /* a HIP call failed; see qlora_last_hip_error() */
+  QLORA_ERR_INIT = 8       /* the codebook could not be derived */
+} qlora_status;
+
+typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
+
+#define QLORA_BLOCK 64       /* weights per first-level constant */
+#define QLORA_DQ_GROUP 256   /* first-level constants per second-level step */
+#define QLORA_MAX_RANK 128   /* largest LoRA rank accepted */
+
+/*
+ * Block-wise NF4 quantization (figures 3 and 4 of "A 65B fine-tune on the
+ * GPU you already have").
+ *   w       [numel] fp32 or bf16 (wdt), the weight in any flat order (row-major
+ *           [N,K] for a Linear layer); 16-byte aligned.
+ *   numel   > 0, multiple of 64.
+ *   packed  [numel/2] out, 16-byte aligned.
+ *   absmax  [numel/64] out, per-block max |w|.
+ * Codes are bit-exact functions of w: v = fp32(w / absmax) with IEEE
+ * division, code = number of thresholds T_j below v, T_j the largest fp32 not
+ * above the exact midpoint of levels j and j+1. An all-zero block codes 7.
+ */
+int qlora_nf4_quantize(const void* w, int wdt, int64_t numel, uint8_t* packed,
+                       float* absmax, void* stream);
+
+/*
+ * Double quantization of the block constants to int8 in groups of 256
+ * (figure 4 of "A 65B fine-tune on the GPU you already have").
+ *   absmax   [nblocks] fp32 >= 0 (from qlora_nf4_quantize).
+ *   nblocks  > 0.
+ *   qscale   [nblocks] int8 out: rne(fp32(absmax / d)), clamped to [-127, 127].
+ *   step     [ceil(nblocks/256)] fp32 out: d = fp32(group max / 127); a group
+ *            whose max is 0 has d = 0 and all q = 0. The last group may be
+ *            partial.
+ */
+int qlora_dq_scales(const float* absmax, int64_t nblocks, int8_t* qscale,
+                    float* step, void* stream);
+
+/*
+ * Standalone dequantization to bf16 (figure 2 of "A 65B fine-tune on the GPU
+ * you already have"): out[i] = bf16_rne(L[code_i] * fp32(q_b * d_g)).
+ *   packed [numel/2], qscale [numel/64], step [ceil(numel/16384)],
+ *   numel > 0 multiple of 64, out [numel] bf16; packed and out 16-byte aligned.
+ * The fused GEMMs below dequantize with exactly this arithmetic.
+ */
+int qlora_nf4_dequant(const uint8_t* packed, const int8_t* qscale,
+                      const float* step, int64_t numel, uint16_t* out,
+                      void* stream);
+
+/*
+ * Workspace (device bytes) that qlora_nf4_lora_fwd (op = 0) or
+ * qlora_nf4_bwd_dx (op = 1) needs for these sizes; 0 when none is needed.
+ * Returns 0 for invalid sizes as well (the call itself reports the error).
+ */
+size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r);
+
+/*
+ * Forward of one QLoRA linear with the dequant fused into the GEMM
+ * (figure 2 of "A 65B fine-tune on the GPU you already have"; "QLoRA
+ * Explained", "What is QLoRA?"; adapters r and lora_alpha as in "QLoRA and
+ * Quantized Training", "In code"):
+ *     y = bf16( x . W'^T + (alpha / r) . t . B^T ),  t = bf16(x . A^T)
+ *   x       [M, K] bf16;  M >= 1, K multiple of 64.
+ *   packed, qscale, step  the stored W [N, K] (N >= 1).
+ *   A       [r, K] bf16, B [N, r] bf16 -- both NULL with r = 0 for no adapter,
+ *           else 1 <= r <= 128.
+ *   alpha   LoRA alpha (the update is scaled by alpha / r).
+ *   y       [M, N] bf16 out.
+ *   workspace / ws_bytes  device scratch of at least
+ *           qlora_workspace_bytes(0, M, N, K, r) bytes, 16-byte aligned
+ *           (may be NULL when that is 0). Its contents are overwritten.
+ * Products are bf16 x bf16 accumulated in fp32. x, packed, y, A, B and the
+ * workspace must be 16-byte aligned.
+ */
+int qlora_nf4_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K,
+                       const uint8_t* packed, const int8_t* qscale,
+                       const float* step, const uint16_t* A, const uint16_t* B,
+                       int r, float alpha, uint16_t* y, void* workspace,
+                       size_t ws_bytes, void* stream);
+
+/*
+ * Backward to the input through the frozen dequantized weight (figure 2 of
+ * "A 65B fine-tune on the GPU you already have": gradients flow through the
+ * frozen 4-bit weights into the adapters; "QLoRA" (techbytebybyte), "Follow
+ * one QLoRA training step"):
+ *     dX = bf16( dY . W' + (alpha / r) . u . A ),  u = bf16(dY . B)
+ *   dy      [M, N] bf16; M >= 1, N >= 1 multiple of 8, K multiple of 64.
+ *   A, B, r, alpha  as in the forward; NULL/0 gives the base term only.
+ *   dx      [M, K] bf16 out.
+ *   workspace / ws_bytes  at least qlora_workspace_bytes(1, M, N, K, r).
+ */
+int qlora_nf4_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K,
+                     const uint8_t* packed, const int8_t* qscale,
+                     const float* step, const uint16_t* A, const uint16_t* B,
+                     int r, float alpha, uint16_t* dx, void* workspace,
+                     size_t ws_bytes, void* stream);
+
+/*
+ * Host copy of the 16 fp32 levels and the 15 fp32 decision thresholds the
+ * kernels use (host pointers). Derived once, in fp64, on first use.
+ */
+int qlora_nf4_codebook(float levels[16], float thresholds[15]);
+
+/* Human-readable name of a qlora_status value (static storage). */
+const char* qlora_status_string(int status);
+
+/* hipError_t of the most recent QLORA_ERR_HIP on the calling thread. */
+int qlora_last_hip_error(void);
+
+/* Library version, e.g. 1 for this ABI. */
+int qlora_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_NF4_H */

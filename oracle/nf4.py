@@ -202,6 +202,19 @@ def dequantize(packed, qscale, step, numel=None):
     return f32_to_bf16_bits(prod)
 
 
+def dequantize_range(packed, qscale, step, lo, hi):
+    """Elements [lo, hi) of ``dequantize`` (lo, hi multiples of 64), computed
+    from those elements' own codes, block constants and group steps only."""
+    assert lo % BLOCK == 0 and hi % BLOCK == 0
+    codes = unpack(np.asarray(packed)[lo // 2:hi // 2])
+    blk = np.arange(lo, hi) // BLOCK
+    q = np.asarray(qscale, dtype=np.int8)[blk].astype(np.float32)
+    d = np.asarray(step, dtype=np.float32)[blk // DQ_GROUP]
+    s = (q * d).astype(np.float32)
+    prod = (codebook()[codes] * s).astype(np.float32)
+    return f32_to_bf16_bits(prod)
+
+
 def quantize_all(w):
     """Convenience: the full storage format (packed, qscale, step, absmax)."""
     packed, absmax = quantize(w)
@@ -217,6 +230,7 @@ __all__ = [
     "BLOCK", "DQ_GROUP", "DQ_QMAX", "normal_quantile", "codebook",
     "level_midpoints", "block_absmax", "normalise", "nearest_code", "pack",
     "unpack", "quantize", "double_quantize", "block_scales",
-    "f32_to_bf16_bits", "bf16_bits_to_f32", "dequantize", "quantize_all",
+    "f32_to_bf16_bits", "bf16_bits_to_f32", "dequantize", "dequantize_range",
+    "quantize_all",
     "n_groups",
 ]

@@ -1,0 +1,9 @@
+"""MI355X-native NF4 dequant-GEMM: the data-parallel hot path of QLoRA.
+
+Block-wise NF4 quantization of a frozen weight, double quantization of its
+block constants, and the fused dequantize-to-bf16 matmuls of one QLoRA linear
+(forward with the LoRA term, backward to the input), as hand-written gfx950
+HIP kernels behind the C ABI declared in include/qlora_nf4.h.
+"""
+from .ops import (NF4Weight, Workspace, bwd_dx, codebook, dequant, dq_scales,  # noqa: F401
+                  lora_fwd, quantize, quantize_weight, workspace_bytes)

@@ -1,0 +1,150 @@
+// C ABI of the NF4 dequant-GEMM library: argument validation, codebook
+// set-up and dispatch to the gfx950 kernels. Every check runs before any HIP
+// call, so a rejected call launches nothing.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qlora_nf4.h"
+#include "codebook.hpp"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return QLORA_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return QLORA_ERR_HIP;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// Shared checks of the stored weight and the adapters.
+int check_weight(const uint8_t* packed, const int8_t* qscale, const float* step) {
+  if (!packed || !qscale || !step) return QLORA_ERR_NULL;
+  if (!aligned16(packed)) return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+
+int check_adapter(const uint16_t* A, const uint16_t* B, int r) {
+  if (r == 0) return (A == nullptr && B == nullptr) ? QLORA_OK : QLORA_ERR_RANK;
+  if (r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_RANK;
+  if (!A || !B) return QLORA_ERR_NULL;
+  if (!aligned16(A) || !aligned16(B)) return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return QLORA_OK;
+  if (!ws || ws_bytes < need) return QLORA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qlora_abi_version(void) { return 1; }
+
+const char* qlora_status_string(int status) {
+  switch (status) {
+    case QLORA_OK: return "ok";
+    case QLORA_ERR_NULL: return "null pointer";
+    case QLORA_ERR_SHAPE: return "bad shape";
+    case QLORA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case QLORA_ERR_RANK: return "bad LoRA rank or adapters";
+    case QLORA_ERR_WORKSPACE: return "workspace missing or too small";
+    case QLORA_ERR_DTYPE: return "unknown dtype";
+    case QLORA_ERR_HIP: return "HIP error";
+    case QLORA_ERR_INIT: return "codebook derivation failed";
+    default: return "unknown status";
+  }
+}
+
+int qlora_last_hip_error(void) { return g_last_hip_error; }
+
+int qlora_nf4_codebook(float levels[16], float thresholds[15]) {
+  if (!levels || !thresholds) return QLORA_ERR_NULL;
+  const qnf4::Codebook* cb = qnf4::codebook();
+  if (!cb) return QLORA_ERR_INIT;
+  for (int i = 0; i < 16; ++i) levels[i] = cb->L[i];
+  for (int i = 0; i < 15; ++i) thresholds[i] = cb->T[i];
+  return QLORA_OK;
+}
+
+size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r) {
+  if ((op != 0 && op != 1) || M < 1 || N < 1 || K < 64 || r < 0 || r > QLORA_MAX_RANK) return 0;
+  return qnf4::ws_layout(op, M, N, K, r).total;
+}
+
+int qlora_nf4_quantize(const void* w, int wdt, int64_t numel, uint8_t* packed, float* absmax, void* stream) {
+  if (!w || !packed || !absmax) return QLORA_ERR_NULL;
+  if (wdt != QLORA_F32 && wdt != QLORA_BF16) return QLORA_ERR_DTYPE;
+  if (numel <= 0 || numel % QLORA_BLOCK != 0) return QLORA_ERR_SHAPE;
+  if (!aligned16(w) || !aligned16(packed)) return QLORA_ERR_ALIGN;
+  const qnf4::Codebook* cb = qnf4::codebook();
+  if (!cb) return QLORA_ERR_INIT;
+  return hip_status(qnf4::launch_quantize(w, wdt, numel, packed, absmax, *cb, as_stream(stream)));
+}
+
+int qlora_dq_scales(const float* absmax, int64_t nblocks, int8_t* qscale, float* step, void* stream) {
+  if (!absmax || !qscale || !step) return QLORA_ERR_NULL;
+  if (nblocks <= 0 || nblocks > (int64_t{1} << 39)) return QLORA_ERR_SHAPE;
+  return hip_status(qnf4::launch_dq_scales(absmax, nblocks, qscale, step, as_stream(stream)));
+}
+
+int qlora_nf4_dequant(const uint8_t* packed, const int8_t* qscale, const float* step, int64_t numel,
+                      uint16_t* out, void* stream) {
+  int st = check_weight(packed, qscale, step);
+  if (st) return st;
+  if (!out) return QLORA_ERR_NULL;
+  if (numel <= 0 || numel % QLORA_BLOCK != 0) return QLORA_ERR_SHAPE;
+  if (!aligned16(out)) return QLORA_ERR_ALIGN;
+  const qnf4::Codebook* cb = qnf4::codebook();
+  if (!cb) return QLORA_ERR_INIT;
+  return hip_status(qnf4::launch_dequant(packed, qscale, step, numel, out, *cb, as_stream(stream)));
+}
+
+int qlora_nf4_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
+                       const int8_t* qscale, const float* step, const uint16_t* A, const uint16_t* B, int r,
+                       float alpha, uint16_t* y, void* workspace, size_t ws_bytes, void* stream) {
+  if (!x || !y) return QLORA_ERR_NULL;
+  int st = check_weight(packed, qscale, step);
+  if (st) return st;
+  if (M < 1 || N < 1 || K < 64 || K % QLORA_BLOCK != 0) return QLORA_ERR_SHAPE;
+  if (M > (int64_t{1} << 31) || N > (int64_t{1} << 31) || K > (int64_t{1} << 31)) return QLORA_ERR_SHAPE;
+  st = check_adapter(A, B, r);
+  if (st) return st;
+  if (!aligned16(x) || !aligned16(y)) return QLORA_ERR_ALIGN;
+  st = check_ws(workspace, ws_bytes, qnf4::ws_layout(0, M, N, K, r).total);
+  if (st) return st;
+  const qnf4::Codebook* cb = qnf4::codebook();
+  if (!cb) return QLORA_ERR_INIT;
+  return hip_status(qnf4::launch_lora_fwd(x, M, N, K, packed, qscale, step, A, B, r, alpha, y, workspace, *cb,
+                                          as_stream(stream)));
+}
+
+int qlora_nf4_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
+                     const int8_t* qscale, const float* step, const uint16_t* A, const uint16_t* B, int r,
+                     float alpha, uint16_t* dx, void* workspace, size_t ws_bytes, void* stream) {
+  if (!dy || !dx) return QLORA_ERR_NULL;
+  int st = check_weight(packed, qscale, step);
+  if (st) return st;
+  if (M < 1 || N < 1 || N % 8 != 0 || K < 64 || K % QLORA_BLOCK != 0) return QLORA_ERR_SHAPE;
+  if (M > (int64_t{1} << 31) || N > (int64_t{1} << 31) || K > (int64_t{1} << 31)) return QLORA_ERR_SHAPE;
+  st = check_adapter(A, B, r);
+  if (st) return st;
+  if (!aligned16(dy) || !aligned16(dx)) return QLORA_ERR_ALIGN;
+  st = check_ws(workspace, ws_bytes, qnf4::ws_layout(1, M, N, K, r).total);
+  if (st) return st;
+  const qnf4::Codebook* cb = qnf4::codebook();
+  if (!cb) return QLORA_ERR_INIT;
+  return hip_status(qnf4::launch_bwd_dx(dy, M, N, K, packed, qscale, step, A, B, r, alpha, dx, workspace, *cb,
+                                        as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// Host-side launchers of the gfx950 kernels and the launch plan they share
+// with the workspace query. Sizes are validated by the C ABI layer before any
+// of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "codebook.hpp"
+
+namespace qnf4 {
+
+// M at or below this uses the GEMV-shaped kernels (decode shapes).
+constexpr int64_t kSmallM = 16;
+
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+inline size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+// LoRA rank padded to the 32-deep MFMA contraction used by the epilogues.
+inline int64_t rank_pad(int r) { return round_up(r, 32); }
+
+// Number of K-slices the rank-r down-projection t = in . W^T is split into
+// (fp32 partials summed by the consumer). One slice for the large-M path.
+inline int64_t lora_splits(int64_t M, int64_t Kc) {
+  if (M > kSmallM) return 1;
+  const int64_t s = cdiv(Kc, 64);
+  return s < 16 ? (s < 1 ? 1 : s) : 16;
+}
+
+// Row slices of the small-M backward (fp32 partials of dX).
+inline int64_t bwd_small_splits(int64_t N, int64_t K) {
+  const int64_t ktiles = cdiv(K, 64);
+  int64_t s = cdiv(256, ktiles);
+  const int64_t steps = cdiv(N, 256);
+  if (s > steps) s = steps;
+  if (s < 1) s = 1;
+  return s;
+}
+
+struct WsLayout {
+  size_t lora_off = 0, lora_bytes = 0;    // t or u (bf16 [M][rp], or fp32 partials)
+  size_t part_off = 0, part_bytes = 0;    // small-M backward partials
+  size_t total = 0;
+};
+
+// op 0: forward (lora contraction over K); op 1: backward (over N).
+inline WsLayout ws_layout(int op, int64_t M, int64_t N, int64_t K, int r) {
+  WsLayout w;
+  if (r > 0) {
+    const int64_t rp = rank_pad(r);
+    const int64_t Kc = op == 0 ? K : N;
+    if (M > kSmallM)
+      w.lora_bytes = align256(static_cast<size_t>(M * rp * 2));
+    else
+      w.lora_bytes = align256(static_cast<size_t>(lora_splits(M, Kc) * M * rp * 4));
+  }
+  w.part_off = w.lora_bytes;
+  if (op == 1 && M <= kSmallM)
+    w.part_bytes = align256(static_cast<size_t>(bwd_small_splits(N, K) * M * K * 4));
+  w.total = w.lora_bytes + w.part_bytes;
+  return w;
+}
+
+hipError_t launch_quantize(const void* w, int wdt, int64_t numel, uint8_t* packed, float* absmax,
+                           const Codebook& cb, hipStream_t stream);
+hipError_t launch_dq_scales(const float* absmax, int64_t nblocks, int8_t* qscale, float* step,
+                            hipStream_t stream);
+hipError_t launch_dequant(const uint8_t* packed, const int8_t* qscale, const float* step, int64_t numel,
+                          uint16_t* out, const Codebook& cb, hipStream_t stream);
+
+hipError_t launch_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
+                           const int8_t* qscale, const float* step, const uint16_t* A, const uint16_t* B,
+                           int r, float alpha, uint16_t* y, void* ws, const Codebook& cb,
+                           hipStream_t stream);
+hipError_t launch_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
+                         const int8_t* qscale, const float* step, const uint16_t* A, const uint16_t* B,
+                         int r, float alpha, uint16_t* dx, void* ws, const Codebook& cb,
+                         hipStream_t stream);
+
+}  // namespace qnf4

@@ -1,0 +1,150 @@
+"""PyTorch-facing wrappers of the C ABI (device tensors in, device tensors out).
+
+PyTorch supplies device memory and the current HIP stream; the arithmetic is
+all in the library's kernels. bf16 tensors are passed as their 16-bit
+patterns, which is what the ABI expects.
+"""
+import ctypes
+
+import torch
+
+from . import _lib
+
+BLOCK = 64
+DQ_GROUP = 256
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, dtype, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class NF4Weight:
+    """Stored frozen weight [N, K]: packed codes, int8 scales, fp32 steps."""
+
+    def __init__(self, packed, qscale, step, shape):
+        self.packed, self.qscale, self.step = packed, qscale, step
+        self.shape = tuple(shape)
+
+    @property
+    def nbytes(self):
+        return self.packed.nbytes + self.qscale.nbytes + self.step.nbytes
+
+
+def quantize(w):
+    """fp32 or bf16 weight -> (packed uint8, absmax fp32). Flat block order."""
+    if w.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("weight must be float32 or bfloat16")
+    _need(w, w.dtype, "w")
+    numel = w.numel()
+    packed = torch.empty(numel // 2, dtype=torch.uint8, device=w.device)
+    absmax = torch.empty(numel // BLOCK, dtype=torch.float32, device=w.device)
+    wdt = _lib.F32 if w.dtype == torch.float32 else _lib.BF16
+    _lib.check("qlora_nf4_quantize", _lib.lib().qlora_nf4_quantize(
+        _ptr(w), wdt, numel, _ptr(packed), _ptr(absmax), _stream(w.device)))
+    return packed, absmax
+
+
+def dq_scales(absmax):
+    _need(absmax, torch.float32, "absmax")
+    nb = absmax.numel()
+    q = torch.empty(nb, dtype=torch.int8, device=absmax.device)
+    step = torch.empty((nb + DQ_GROUP - 1) // DQ_GROUP, dtype=torch.float32, device=absmax.device)
+    _lib.check("qlora_dq_scales", _lib.lib().qlora_dq_scales(
+        _ptr(absmax), nb, _ptr(q), _ptr(step), _stream(absmax.device)))
+    return q, step
+
+
+def quantize_weight(w):
+    """Full storage format of a 2-D weight [N, K]: NF4 codes + double-quantized constants."""
+    packed, absmax = quantize(w)
+    q, step = dq_scales(absmax)
+    return NF4Weight(packed, q, step, w.shape)
+
+
+def dequant(qw, out=None):
+    numel = qw.packed.numel() * 2
+    dev = qw.packed.device
+    if out is None:
+        out = torch.empty(qw.shape, dtype=torch.bfloat16, device=dev)
+    _need(out, torch.bfloat16, "out")
+    _lib.check("qlora_nf4_dequant", _lib.lib().qlora_nf4_dequant(
+        _ptr(qw.packed), _ptr(qw.qscale), _ptr(qw.step), numel, _ptr(out), _stream(dev)))
+    return out
+
+
+def workspace_bytes(op, M, N, K, r):
+    return int(_lib.lib().qlora_workspace_bytes(op, M, N, K, r))
+
+
+class Workspace:
+    """Grow-only device scratch buffer reused across calls on one stream."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes):
+        if nbytes == 0:
+            return None
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+def lora_fwd(x, qw, A=None, B=None, alpha=0.0, out=None, ws=None):
+    """y = x . deq(W)^T + (alpha/r) . (x . A^T) . B^T, all bf16 [M, K] -> [M, N]."""
+    _need(x, torch.bfloat16, "x")
+    M, K = x.shape
+    N = qw.shape[0]
+    r = 0 if A is None else A.shape[0]
+    if A is not None:
+        _need(A, torch.bfloat16, "A")
+        _need(B, torch.bfloat16, "B")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    need = workspace_bytes(0, M, N, K, r)
+    wsb = (ws or Workspace(x.device)).get(need)
+    _lib.check("qlora_nf4_lora_fwd", _lib.lib().qlora_nf4_lora_fwd(
+        _ptr(x), M, N, K, _ptr(qw.packed), _ptr(qw.qscale), _ptr(qw.step), _ptr(A), _ptr(B), r,
+        float(alpha), _ptr(out), _ptr(wsb), 0 if wsb is None else wsb.numel(), _stream(x.device)))
+    return out
+
+
+def bwd_dx(dy, qw, A=None, B=None, alpha=0.0, out=None, ws=None):
+    """dX = dY . deq(W) + (alpha/r) . (dY . B) . A, bf16 [M, N] -> [M, K]."""
+    _need(dy, torch.bfloat16, "dy")
+    M, N = dy.shape
+    K = qw.shape[1]
+    r = 0 if A is None else A.shape[0]
+    if A is not None:
+        _need(A, torch.bfloat16, "A")
+        _need(B, torch.bfloat16, "B")
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.bfloat16, device=dy.device)
+    need = workspace_bytes(1, M, N, K, r)
+    wsb = (ws or Workspace(dy.device)).get(need)
+    _lib.check("qlora_nf4_bwd_dx", _lib.lib().qlora_nf4_bwd_dx(
+        _ptr(dy), M, N, K, _ptr(qw.packed), _ptr(qw.qscale), _ptr(qw.step), _ptr(A), _ptr(B), r,
+        float(alpha), _ptr(out), _ptr(wsb), 0 if wsb is None else wsb.numel(), _stream(dy.device)))
+    return out
+
+
+def codebook():
+    """(levels[16], thresholds[15]) as the kernels use them, host floats."""
+    L = (ctypes.c_float * 16)()
+    T = (ctypes.c_float * 15)()
+    _lib.check("qlora_nf4_codebook", _lib.lib().qlora_nf4_codebook(L, T))
+    return list(L), list(T)

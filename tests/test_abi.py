@@ -1,0 +1,120 @@
+"""CPU checks of the C-ABI library: it loads, exports every symbol the header
+declares, derives the same codebook as the oracle bit for bit, sizes its
+workspace consistently, and rejects bad arguments with status codes before
+launching anything (no GPU is touched by these calls)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from qlora_dequant_gemm_amd import _lib, ops
+from oracle import nf4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora_nf4.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 10
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(n for n, _, _ in _lib.SIGNATURES) == names
+
+
+def test_abi_version_and_status_strings():
+    L = _lib.lib()
+    assert L.qlora_abi_version() == 1
+    for code in range(9):
+        assert L.qlora_status_string(code)
+    assert L.qlora_status_string(99) == b"unknown status"
+
+
+def test_codebook_bitwise_equals_oracle():
+    levels, thresholds = ops.codebook()
+    L = np.array(levels, np.float32)
+    assert np.array_equal(L.view(np.uint32), nf4.codebook().view(np.uint32))
+    # thresholds: largest fp32 not above each exact midpoint
+    mids = nf4.level_midpoints()
+    T = np.array(thresholds, np.float32)
+    assert np.all(T.astype(np.float64) <= mids)
+    assert np.all(np.nextafter(T, np.float32(2)).astype(np.float64) > mids)
+
+
+def test_workspace_sizes():
+    ws = ops.workspace_bytes
+    assert ws(0, 4096, 11008, 4096, 0) == 0
+    assert ws(0, 4096, 11008, 4096, 16) == 4096 * 32 * 2          # bf16 t, rank padded to 32
+    assert ws(0, 16, 4096, 4096, 16) == 16 * 16 * 32 * 4          # 16 K-slices of fp32 partials
+    assert ws(1, 16, 4096, 4096, 0) > 0                           # small-M backward partials
+    assert ws(1, 4096, 4096, 11008, 0) == 0
+    assert ws(2, 16, 16, 64, 0) == 0 and ws(0, 0, 16, 64, 0) == 0
+    for op in (0, 1):
+        assert ws(op, 16, 8, 64, 8) % 256 == 0
+
+
+V = ctypes.c_void_p
+FAKE = V(0x10000)          # a 16-byte aligned non-null address that is never dereferenced
+ODD = V(0x10008)           # not 16-byte aligned
+
+
+def _fwd(x=FAKE, M=16, N=64, K=64, packed=FAKE, q=FAKE, step=FAKE, A=V(0), B=V(0), r=0, alpha=0.0,
+         y=FAKE, ws=V(0), wsb=0):
+    return _lib.lib().qlora_nf4_lora_fwd(x, M, N, K, packed, q, step, A, B, r, alpha, y, ws, wsb, V(0))
+
+
+def _bwd(dy=FAKE, M=16, N=64, K=64, packed=FAKE, q=FAKE, step=FAKE, A=V(0), B=V(0), r=0, alpha=0.0,
+         dx=FAKE, ws=V(0), wsb=None):
+    if wsb is None:
+        wsb = ops.workspace_bytes(1, M, N, K, r)
+        ws = FAKE if wsb else V(0)
+    return _lib.lib().qlora_nf4_bwd_dx(dy, M, N, K, packed, q, step, A, B, r, alpha, dx, ws, wsb, V(0))
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(x=V(0)), 1), (dict(y=V(0)), 1), (dict(packed=V(0)), 1), (dict(q=V(0)), 1),
+    (dict(step=V(0)), 1),
+    (dict(M=0), 2), (dict(N=0), 2), (dict(K=0), 2), (dict(K=96), 2), (dict(K=32), 2),
+    (dict(x=ODD), 3), (dict(y=ODD), 3), (dict(packed=ODD), 3),
+    (dict(r=8), 1), (dict(r=8, A=FAKE), 1), (dict(A=FAKE), 4), (dict(r=-1), 4),
+    (dict(r=129, A=FAKE, B=FAKE), 4),
+    (dict(r=8, A=ODD, B=FAKE, ws=FAKE, wsb=1 << 20), 3),
+    (dict(r=8, A=FAKE, B=FAKE), 5), (dict(r=8, A=FAKE, B=FAKE, ws=FAKE, wsb=16), 5),
+    (dict(r=8, A=FAKE, B=FAKE, ws=ODD, wsb=1 << 20), 3),
+])
+def test_forward_rejects_bad_arguments(kwargs, status):
+    assert _fwd(**kwargs) == status
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dy=V(0)), 1), (dict(dx=V(0)), 1), (dict(N=12), 2), (dict(N=0), 2), (dict(K=100), 2),
+    (dict(dy=ODD), 3), (dict(dx=ODD), 3), (dict(r=4, A=FAKE), 1),
+    (dict(ws=V(0), wsb=0), 5),
+])
+def test_backward_rejects_bad_arguments(kwargs, status):
+    assert _bwd(**kwargs) == status
+
+
+def test_quantize_dq_dequant_reject_bad_arguments():
+    L = _lib.lib()
+    assert L.qlora_nf4_quantize(V(0), 0, 64, FAKE, FAKE, V(0)) == 1
+    assert L.qlora_nf4_quantize(FAKE, 0, 65, FAKE, FAKE, V(0)) == 2
+    assert L.qlora_nf4_quantize(FAKE, 0, 0, FAKE, FAKE, V(0)) == 2
+    assert L.qlora_nf4_quantize(FAKE, 5, 64, FAKE, FAKE, V(0)) == 6
+    assert L.qlora_nf4_quantize(ODD, 0, 64, FAKE, FAKE, V(0)) == 3
+    assert L.qlora_dq_scales(FAKE, 0, FAKE, FAKE, V(0)) == 2
+    assert L.qlora_dq_scales(V(0), 4, FAKE, FAKE, V(0)) == 1
+    assert L.qlora_nf4_dequant(FAKE, FAKE, FAKE, 100, FAKE, V(0)) == 2
+    assert L.qlora_nf4_dequant(FAKE, FAKE, FAKE, 64, ODD, V(0)) == 3
+    assert L.qlora_nf4_dequant(FAKE, V(0), FAKE, 64, FAKE, V(0)) == 1
+    a = (ctypes.c_float * 16)()
+    assert L.qlora_nf4_codebook(a, None) == 1

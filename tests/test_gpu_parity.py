@@ -1,0 +1,297 @@
+"""GPU parity of the HIP path against the CPU oracle (run on an MI355X).
+
+Bars (stated per check):
+  * codes (packed nibbles), first-level absmax, int8 scales, fp32 steps and the
+    standalone dequantized bf16: bit-exact;
+  * forward y and backward dX: relative Frobenius error <= 1e-2 against the
+    fp64 oracle (the stated tolerance), and <= 5e-3, the bound bf16 output
+    rounding (unit roundoff 2^-8) plus fp32 accumulation allows;
+  * one-hot inputs (a single product per output, no adapter): bit-exact;
+  * the LoRA term alone (all-zero weight): relative Frobenius <= 1e-2.
+The oracle quantizes the same seeded inputs itself: nothing it is given comes
+from the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import gemm, nf4
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+TIGHT = 5e-3
+
+
+@pytest.fixture(scope="module")
+def qops():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from qlora_dequant_gemm_amd import ops
+    return ops
+
+
+def dev(a):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if a.dtype == np.uint16:
+        t = t.view(torch.bfloat16)
+    return t.cuda()
+
+
+def host_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def rel_fro(got, ref):
+    return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+
+
+def to_f64(bits):
+    return gemm.bf16_to_f64(bits)
+
+
+def gpu_quant(ops, w):
+    qw = ops.quantize_weight(dev(w))
+    return qw
+
+
+# ---------------------------------------------------------------------------
+# quantize / double-quant / dequant: bit-exact
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("N,K,seed", [(256, 256, 0), (3, 64, 1), (5, 192, 2), (300, 320, 3),
+                                      (1000, 1024, 4)])
+def test_quantize_dq_dequant_bit_exact_small(qops, N, K, seed):
+    w = synth.weight(N, K, seed)
+    if seed == 3:
+        w[7, :64] = 0.0                           # an all-zero block
+        w[9, 64:128] = -w[9, 64:128]
+    packed, absmax = qops.quantize(dev(w))
+    q, step = qops.dq_scales(absmax)
+    torch.cuda.synchronize()
+    opk, oa = nf4.quantize(w)
+    oq, ostep = nf4.double_quantize(oa)
+    assert np.array_equal(packed.cpu().numpy(), opk)
+    assert np.array_equal(absmax.cpu().numpy().view(np.uint32), oa.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), oq)
+    assert np.array_equal(step.cpu().numpy().view(np.uint32), ostep.view(np.uint32))
+    qw = qops.NF4Weight(packed, q, step, (N, K))
+    out = host_bits(qops.dequant(qw)).reshape(-1)
+    assert np.array_equal(out, nf4.dequantize(opk, oq, ostep))
+
+
+def test_quantize_bf16_input_bit_exact(qops):
+    w = synth.to_bf16_bits(synth.weight(128, 512, 7))
+    packed, absmax = qops.quantize(dev(w))
+    opk, oa = nf4.quantize(w)
+    assert np.array_equal(packed.cpu().numpy(), opk)
+    assert np.array_equal(absmax.cpu().numpy(), oa)
+
+
+def test_exact_level_weights_code_to_themselves(qops):
+    L = nf4.codebook()
+    c = np.tile(np.arange(16), 64 * 16)
+    w = (L[c] * np.float32(2.0 ** -6)).astype(np.float32).reshape(64, 256)
+    packed, _ = qops.quantize(dev(w))
+    assert np.array_equal(nf4.unpack(packed.cpu().numpy()), c.astype(np.uint8))
+
+
+@pytest.mark.parametrize("name", ["7b_attn", "7b_mlp_up"])
+def test_quantize_full_size_bit_exact(qops, name):
+    c = synth.CONFIGS[name]
+    w = synth.weight(c["N"], c["K"], c["seeds"]["w"])
+    qw = gpu_quant(qops, w)
+    opk, oq, ostep, _ = nf4.quantize_all(w)
+    assert np.array_equal(qw.packed.cpu().numpy(), opk)
+    assert np.array_equal(qw.qscale.cpu().numpy(), oq)
+    assert np.array_equal(qw.step.cpu().numpy().view(np.uint32), ostep.view(np.uint32))
+    out = host_bits(qops.dequant(qw)).reshape(-1)
+    assert np.array_equal(out, nf4.dequantize(opk, oq, ostep))
+
+
+def test_quantize_65b_outliers_sampled_groups_bit_exact(qops):
+    """65B up-projection with 0.1% x10 outliers: DQ groups are independent, so
+    the oracle checks 64 random groups (and their blocks) exactly."""
+    c = synth.CONFIGS["65b_up"]
+    s = c["seeds"]
+    w = synth.weight(c["N"], c["K"], s["w"], c["outliers"], s["outliers"])
+    qw = gpu_quant(qops, w)
+    packed = qw.packed.cpu().numpy()
+    q = qw.qscale.cpu().numpy()
+    step = qw.step.cpu().numpy()
+    flat = w.reshape(-1)
+    ng = step.size
+    rng = np.random.Generator(np.random.PCG64(99))
+    for g in sorted(rng.choice(ng, 64, replace=False)):
+        lo, hi = g * 16384, (g + 1) * 16384
+        opk, oa = nf4.quantize(flat[lo:hi])
+        oq, ostep = nf4.double_quantize(oa)
+        assert np.array_equal(packed[lo // 2:hi // 2], opk)
+        assert np.array_equal(q[lo // 64:hi // 64], oq)
+        assert step[g].view(np.uint32) == ostep[0].view(np.uint32)
+
+
+# ---------------------------------------------------------------------------
+# forward / backward, element by element at small ragged sizes
+# ---------------------------------------------------------------------------
+FWD_CASES = [
+    # M, N, K, r, alpha, seed
+    (16, 256, 256, 8, 16.0, 0),        # the tiny config
+    (1, 4096 // 16, 512, 16, 32.0, 10),
+    (4, 300, 320, 16, 32.0, 11),
+    (5, 37, 64, 5, 7.0, 12),           # odd rank: element loads of B
+    (16, 520, 768, 128, 16.0, 13),
+    (17, 300, 320, 16, 32.0, 14),      # first M of the tiled path
+    (300, 520, 320, 8, 16.0, 15),      # 2 x 3 tiles, ragged in M and N
+    (513, 256, 128, 64, 16.0, 16),
+    (260, 1, 64, 0, 0.0, 17),          # N = 1, no adapter
+]
+
+
+def _fwd_case(ops, M, N, K, r, alpha, seed):
+    w = synth.weight(N, K, seed)
+    x = synth.activations(M, K, seed + 1)
+    A, B = synth.adapters(N, K, r, seed + 2, seed + 3) if r else (None, None)
+    qw = gpu_quant(ops, w)
+    y = ops.lora_fwd(dev(x), qw, dev(A) if r else None, dev(B) if r else None, alpha)
+    got = to_f64(host_bits(y))
+    opk, oq, ostep, _ = nf4.quantize_all(w)
+    wd = nf4.dequantize(opk, oq, ostep).reshape(N, K)
+    ref = gemm.lora_forward(x, wd, A, B, alpha, r)
+    return got, ref
+
+
+@pytest.mark.parametrize("M,N,K,r,alpha,seed", FWD_CASES)
+def test_forward_parity(qops, M, N, K, r, alpha, seed):
+    got, ref = _fwd_case(qops, M, N, K, r, alpha, seed)
+    e = rel_fro(got, ref)
+    assert e <= TOL and e <= TIGHT, e
+
+
+BWD_CASES = [
+    (16, 256, 256, 8, 16.0, 20),
+    (1, 64, 512, 16, 32.0, 21),
+    (4, 296, 320, 16, 32.0, 22),       # N multiple of 8, not of 64
+    (16, 8, 64, 4, 8.0, 23),
+    (16, 1000, 768, 128, 16.0, 24),
+    (17, 296, 320, 16, 32.0, 25),
+    (300, 520, 320, 8, 16.0, 26),
+    (513, 136, 576, 64, 16.0, 27),
+    (260, 64, 64, 0, 0.0, 28),
+]
+
+
+def _bwd_case(ops, M, N, K, r, alpha, seed):
+    w = synth.weight(N, K, seed)
+    dy = synth.activations(M, N, seed + 1)
+    A, B = synth.adapters(N, K, r, seed + 2, seed + 3) if r else (None, None)
+    qw = gpu_quant(ops, w)
+    dx = ops.bwd_dx(dev(dy), qw, dev(A) if r else None, dev(B) if r else None, alpha)
+    got = to_f64(host_bits(dx))
+    opk, oq, ostep, _ = nf4.quantize_all(w)
+    wd = nf4.dequantize(opk, oq, ostep).reshape(N, K)
+    ref = gemm.backward_dx(dy, wd, A, B, alpha, r)
+    return got, ref
+
+
+@pytest.mark.parametrize("M,N,K,r,alpha,seed", BWD_CASES)
+def test_backward_parity(qops, M, N, K, r, alpha, seed):
+    got, ref = _bwd_case(qops, M, N, K, r, alpha, seed)
+    e = rel_fro(got, ref)
+    assert e <= TOL and e <= TIGHT, e
+
+
+@pytest.mark.parametrize("M,N,K", [(4, 48, 128), (16, 200, 320), (40, 300, 320), (300, 64, 576)])
+def test_one_hot_forward_bit_exact(qops, M, N, K):
+    """x row m = e_{k_m}: y[m, n] = W'[n, k_m], a single product per output."""
+    w = synth.weight(N, K, 40 + M)
+    ks = (np.arange(M) * 37 + 5) % K
+    x = np.zeros((M, K), np.float32)
+    x[np.arange(M), ks] = 1.0
+    xb = synth.to_bf16_bits(x)
+    qw = gpu_quant(qops, w)
+    y = host_bits(qops.lora_fwd(dev(xb), qw))
+    opk, oq, ostep, _ = nf4.quantize_all(w)
+    wd = nf4.dequantize(opk, oq, ostep).reshape(N, K)
+    want = wd[:, ks].T
+    # -0 and +0 are the same product; compare values
+    assert np.array_equal(to_f64(y), to_f64(np.ascontiguousarray(want)))
+
+
+@pytest.mark.parametrize("M,N,K", [(4, 48, 128), (16, 200, 320), (40, 296, 320), (300, 64, 576)])
+def test_one_hot_backward_bit_exact(qops, M, N, K):
+    """dY row m = e_{n_m}: dX[m, k] = W'[n_m, k]."""
+    w = synth.weight(N, K, 60 + M)
+    ns = (np.arange(M) * 29 + 3) % N
+    dy = np.zeros((M, N), np.float32)
+    dy[np.arange(M), ns] = 1.0
+    qw = gpu_quant(qops, w)
+    dx = host_bits(qops.bwd_dx(dev(synth.to_bf16_bits(dy)), qw))
+    opk, oq, ostep, _ = nf4.quantize_all(w)
+    wd = nf4.dequantize(opk, oq, ostep).reshape(N, K)
+    assert np.array_equal(to_f64(dx), to_f64(np.ascontiguousarray(wd[ns])))
+
+
+@pytest.mark.parametrize("M", [4, 300])
+def test_lora_term_alone(qops, M):
+    """All-zero weight: every block constant is 0, so y is the LoRA term only."""
+    N, K, r, alpha = 200, 320, 16, 32.0
+    w = np.zeros((N, K), np.float32)
+    x = synth.activations(M, K, 80)
+    A, B = synth.adapters(N, K, r, 81, 82)
+    qw = gpu_quant(qops, w)
+    got = to_f64(host_bits(qops.lora_fwd(dev(x), qw, dev(A), dev(B), alpha)))
+    ref = gemm.lora_forward(x, np.zeros((N, K), np.uint16), A, B, alpha, r)
+    assert np.abs(ref).max() > 0
+    assert rel_fro(got, ref) <= TOL
+    dy = synth.activations(M, N, 83)
+    got = to_f64(host_bits(qops.bwd_dx(dev(dy), qw, dev(A), dev(B), alpha)))
+    ref = gemm.backward_dx(dy, np.zeros((N, K), np.uint16), A, B, alpha, r)
+    assert rel_fro(got, ref) <= TOL
+
+
+def test_determinism(qops):
+    M, N, K, r = 300, 520, 320, 8
+    w = synth.weight(N, K, 90)
+    x = dev(synth.activations(M, K, 91))
+    A, B = (dev(a) for a in synth.adapters(N, K, r, 92, 93))
+    qw = gpu_quant(qops, w)
+    y1 = host_bits(qops.lora_fwd(x, qw, A, B, 16.0))
+    y2 = host_bits(qops.lora_fwd(x, qw, A, B, 16.0))
+    assert np.array_equal(y1, y2)
+    dy = dev(synth.activations(M, N, 94))
+    d1 = host_bits(qops.bwd_dx(dy, qw, A, B, 16.0))
+    d2 = host_bits(qops.bwd_dx(dy, qw, A, B, 16.0))
+    assert np.array_equal(d1, d2)
+
+
+# ---------------------------------------------------------------------------
+# full-size configs: sampled outputs computed one by one by the oracle
+# ---------------------------------------------------------------------------
+FULL = [("7b_attn", 1), ("7b_attn", 4), ("7b_attn", 16), ("7b_mlp_up", None),
+        ("7b_mlp_down", None), ("65b_up", None), ("65b_attn", None)]
+
+
+@pytest.mark.parametrize("name,M", FULL)
+def test_full_size_sampled(qops, name, M):
+    inp = synth.config_inputs(name, M)
+    M, N, K, r, alpha = inp["M"], inp["N"], inp["K"], inp["r"], inp["alpha"]
+    w = inp["w"]
+    qw = gpu_quant(qops, w)
+    y = host_bits(qops.lora_fwd(dev(inp["x"]), qw, dev(inp["A"]), dev(inp["B"]), alpha))
+    dx = host_bits(qops.bwd_dx(dev(inp["dy"]), qw, dev(inp["A"]), dev(inp["B"]), alpha))
+    del qw
+    torch.cuda.empty_cache()
+    opk, oq, ostep, _ = nf4.quantize_all(w)
+    rng = np.random.Generator(np.random.PCG64(7))
+    ns = rng.integers(0, N, 64)
+    ms = rng.integers(0, M, 64)
+    ks = rng.integers(0, K, 64)
+    rows = {int(n): nf4.dequantize_range(opk, oq, ostep, int(n) * K, (int(n) + 1) * K) for n in set(ns)}
+    ref = gemm.lora_forward_at(ms, ns, inp["x"], lambda n: rows[int(n)], inp["A"], inp["B"], alpha, r)
+    got = to_f64(y[ms, ns])
+    assert rel_fro(got, ref) <= TIGHT
+    wd = nf4.dequantize(opk, oq, ostep).reshape(N, K)
+    ref = gemm.backward_dx_at(ms, ks, inp["dy"], lambda k: wd[:, int(k)], inp["A"], inp["B"], alpha, r)
+    got = to_f64(dx[ms, ks])
+    assert rel_fro(got, ref) <= TIGHT

@@ -178,3 +178,12 @@ def test_dequant_negative_zero_for_zero_constant():
     packed, q, step, _ = nf4.quantize_all(np.zeros(64, np.float32))
     out = nf4.dequantize(packed, q, step)
     assert np.all(out == 0x8000)                    # bf16(L[7] * 0) = -0
+
+
+def test_dequantize_range_agrees_with_whole_array():
+    rng = np.random.Generator(np.random.PCG64(13))
+    w = (rng.standard_normal(64 * 700) * 0.02).astype(np.float32)
+    packed, q, step, _ = nf4.quantize_all(w)
+    full = nf4.dequantize(packed, q, step)
+    for lo, hi in [(0, 64), (64 * 250, 64 * 260), (64 * 511, 64 * 700)]:
+        assert np.array_equal(nf4.dequantize_range(packed, q, step, lo, hi), full[lo:hi])
