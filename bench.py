@@ -1,0 +1,321 @@
+#!/usr/bin/env python3
+"""Benchmark of the NF4 dequant-GEMM hot path on one MI355X.
+
+Default workload: the 7B-shaped attention projection W [4096, 4096] with
+NF4 + double quantization, LoRA r=16 (alpha 32), decode shapes. One step is
+one pass of the whole hot path over one batch of synthetic input:
+  quantize W (fp32 -> NF4 codes + block absmax) -> double-quantize constants
+  -> fused dequant forward at M = 1, 4 and 16 (each: LoRA down-projection +
+     dequant-GEMV with the LoRA epilogue)
+  -> fused dequant backward dX at M = 16.
+The dequantization itself happens inside the fused kernels. Weight copies are
+rotated (more of them than the 256 MB last-level cache holds) so the fused
+kernels stream their NF4 weights from HBM: each step quantizes copy c and runs
+the matmuls on copy c + C/2, which was written long before.
+
+value = algorithmic bytes of the step / step time (GB/s); the algorithmic
+bytes are what the method must read and write once: fp32 W read + stored
+format written for the quantize, and per matmul the stored weight
+(0.515869 bytes/param), the adapters and the activations in and out.
+
+Other shapes (--config 7b_mlp_up, 65b_up, ...) run the MFMA-bound training
+path (forward + backward dX at M = 4096 / 2048) and report TFLOP/s.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFS = 2500.0     # MI355X dense bf16 MFMA, vendor figure
+NF4_BYTES_PER_PARAM = 0.5 + 1 / 64 + 4 / 16384
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="7b_attn")
+    p.add_argument("--copies", type=int, default=0, help="weight copies rotated (0 = auto)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle CPU time")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work
+# ---------------------------------------------------------------------------
+def quantize_bytes(N, K):
+    return N * K * (4 + NF4_BYTES_PER_PARAM)
+
+
+def matmul_bytes(M, N, K, r, op):
+    weight = N * K * NF4_BYTES_PER_PARAM
+    adapters = 2 * r * (K + N)
+    acts = 2 * M * K + 2 * M * N
+    return weight + adapters + acts
+
+
+def matmul_flops(M, N, K, r):
+    return 2 * M * N * K + 2 * M * r * (K + N)
+
+
+# ---------------------------------------------------------------------------
+# GPU workload
+# ---------------------------------------------------------------------------
+class Workload:
+    def __init__(self, name, copies):
+        import torch
+        import synth
+        from qlora_dequant_gemm_amd import ops
+        self.torch, self.ops = torch, ops
+        c = synth.CONFIGS[name]
+        self.name = name
+        self.N, self.K, self.r, self.alpha = c["N"], c["K"], c["r"], c["alpha"]
+        self.decode = max(c["M"]) <= 16
+        self.Ms = list(c["M"])
+        s = c["seeds"]
+        dev = "cuda"
+        N, K, r = self.N, self.K, self.r
+        w = synth.weight(N, K, s["w"], c.get("outliers", 0.0), s.get("outliers"))
+        w_t = torch.from_numpy(w).to(dev)
+        nbytes_w = w.nbytes
+        if copies <= 0:
+            # enough fp32 + NF4 copies to exceed the 256 MB last-level cache twice
+            copies = int(min(64, max(4, np.ceil(2 * 256e6 / (nbytes_w + N * K * NF4_BYTES_PER_PARAM)))))
+            copies += copies % 2
+        self.C = copies
+        # distinct weights per copy (scaled by 1 + c/1024, same distribution shape)
+        self.w = [w_t * (1.0 + i / 1024.0) for i in range(copies)]
+        self.qw = [ops.quantize_weight(wi) for wi in self.w]
+        bf = lambda a: torch.from_numpy(a).view(torch.bfloat16).to(dev)
+        A, B = synth.adapters(N, K, r, s["A"], s["B"])
+        self.A, self.B = bf(A), bf(B)
+        self.x = {M: bf(synth.activations(M, K, s["x"])) for M in self.Ms}
+        self.dy = {M: bf(synth.activations(M, N, s["dy"])) for M in self.Ms}
+        self.bwd_M = [max(self.Ms)]
+        self.y = {M: torch.empty((M, N), dtype=torch.bfloat16, device=dev) for M in self.Ms}
+        self.dx = {M: torch.empty((M, K), dtype=torch.bfloat16, device=dev) for M in self.bwd_M}
+        self.ws = ops.Workspace(dev)
+        self.ws.get(max(ops.workspace_bytes(op, M, N, K, r) for op in (0, 1) for M in self.Ms))
+        self.absmax_c = torch.empty(N * K // 64, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+
+    # the calls of one step, in order, as (label, fn)
+    def calls(self, step):
+        wl = self
+        c = step % self.C
+        u = (c + self.C // 2) % self.C
+        out = []
+        qw_dst = self.qw[c]
+
+        def quant():
+            wl.ops.quantize(self.w[c], packed=qw_dst.packed, absmax=self.absmax_c)
+
+        def dq():
+            wl.ops.dq_scales(self.absmax_c, q=qw_dst.qscale, step=qw_dst.step)
+
+        out.append(("quantize", quant))
+        out.append(("dq_scales", dq))
+        for M in self.Ms:
+            out.append((f"fwd_M{M}", lambda M=M: wl.ops.lora_fwd(self.x[M], self.qw[u], self.A, self.B,
+                                                                   self.alpha, out=self.y[M], ws=self.ws)))
+        for M in self.bwd_M:
+            out.append((f"bwd_M{M}", lambda M=M: wl.ops.bwd_dx(self.dy[M], self.qw[u], self.A, self.B,
+                                                                 self.alpha, out=self.dx[M], ws=self.ws)))
+        return out
+
+    def work(self):
+        """{label: (bytes, flops)} algorithmic work per call."""
+        N, K, r = self.N, self.K, self.r
+        wk = {"quantize": (N * K * (4 + 0.5 + 4 / 64), 0.0),
+              "dq_scales": (N * K * (4 / 64 + 1 / 64) + 4 * N * K / 16384, 0.0)}
+        for M in self.Ms:
+            wk[f"fwd_M{M}"] = (matmul_bytes(M, N, K, r, 0), matmul_flops(M, N, K, r))
+        for M in self.bwd_M:
+            wk[f"bwd_M{M}"] = (matmul_bytes(M, N, K, r, 1), matmul_flops(M, N, K, r))
+        return wk
+
+
+def run_gpu(args):
+    """Step time from graph replays; per-call kernel times from an eager pass."""
+    import torch
+    wl = Workload(args.config, args.copies)
+    labels = [lab for lab, _ in wl.calls(0)]
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for s in range(args.warmup):
+            for _, fn in wl.calls(s):
+                fn()
+    torch.cuda.synchronize()
+    # one graph per weight-copy phase of the rotation; each holds one full step
+    graphs = []
+    for c in range(wl.C):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _, fn in wl.calls(c):
+                fn()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for s in range(args.warmup):
+        graphs[s % wl.C].replay()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for s in range(args.steps):
+            graphs[(args.warmup + s) % wl.C].replay()
+        end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / args.steps
+
+    # per-call durations: a GPU-side sleep lets the host enqueue a whole step
+    # before the GPU starts it, so the events bracket kernel execution only
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(labels) + 1)] for _ in range(args.steps)]
+    with torch.cuda.stream(stream):
+        for s in range(args.steps):
+            calls = wl.calls(args.warmup + s)
+            torch.cuda._sleep(2_000_000)
+            ev[s][0].record(stream)
+            for i, (_, fn) in enumerate(calls):
+                fn()
+                ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    per_call = {lab: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
+                for i, lab in enumerate(labels)}
+    return wl, ms_step, per_call, wall
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, timed on the host on a bounded sample
+# ---------------------------------------------------------------------------
+def cpu_baseline(args, wl):
+    import synth
+    from oracle import gemm, nf4
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    cores = len(os.sched_getaffinity(0))
+    c = synth.CONFIGS[wl.name]
+    s = c["seeds"]
+    N, K, r, alpha = wl.N, wl.K, wl.r, wl.alpha
+    # sample: whole rows of W (a row-slice is a valid smaller instance of the
+    # same per-row work), sized to about --cpu-seconds of oracle time
+    w = synth.weight(N, K, s["w"], c.get("outliers", 0.0), s.get("outliers"))
+    A, B = synth.adapters(N, K, r, s["A"], s["B"])
+    rows = min(N, 256)
+    xs = {M: synth.activations(M, K, s["x"]) for M in wl.Ms}
+    dys = {M: synth.activations(M, N, s["dy"]) for M in wl.bwd_M}
+    total_bytes = 0.0
+    t_total = 0.0
+    reps = 0
+    while True:
+        n0 = (reps * rows) % N
+        sl = slice(n0, min(N, n0 + rows))
+        ws = w[sl]
+        nrow = ws.shape[0]
+        t = time.perf_counter()
+        packed, q, step, _ = nf4.quantize_all(ws)
+        wd = nf4.dequantize(packed, q, step).reshape(nrow, K)
+        for M in wl.Ms:
+            gemm.lora_forward(xs[M], wd, A, B[sl], alpha, r)
+        for M in wl.bwd_M:
+            gemm.backward_dx(dys[M][:, sl], wd, A, B[sl], alpha, r)
+        t_total += time.perf_counter() - t
+        frac = nrow / N
+        wk = wl.work()
+        total_bytes += frac * sum(b for b, _ in wk.values())
+        reps += 1
+        if t_total >= args.cpu_seconds or reps * rows >= 4 * N:
+            break
+        if t_total < args.cpu_seconds / 8 and rows < N:
+            rows = min(N, rows * 2)
+    return {"value": total_bytes / t_total / 1e9, "unit": "GB/s", "cores": int(max(1, blas_threads)),
+            "host_cores": cores, "kind": "oracle",
+            "sample": f"{reps} oracle passes over row slices of W ({rows} rows each of {N}x{K}; "
+                      f"quantize+DQ+dequant single-threaded numpy, fp64 matmuls on {blas_threads} BLAS "
+                      f"threads); {t_total:.1f} s of CPU time, scaled to the same algorithmic bytes"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        sys.stderr.write("bench.py measures one GPU only: the NF4 dequant-GEMM hot path runs on a single "
+                         "MI355X here; --gpus N > 1 is not supported.\n")
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        sys.stderr.write("bench.py needs a GPU\n")
+        sys.exit(1)
+    wl, ms_step, per_call, wall = run_gpu(args)
+    wk = wl.work()
+    step_bytes = sum(b for b, _ in wk.values())
+    step_flops = sum(f for _, f in wk.values())
+    kernels = {}
+    for lab, ms in per_call.items():
+        b, f = wk[lab]
+        kernels[lab] = {"ms": round(ms, 5), "GB/s": round(b / ms / 1e6, 1),
+                        "hbm_frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4)}
+        if f:
+            kernels[lab]["TFLOP/s"] = round(f / ms / 1e9, 2)
+    dom = max(per_call, key=per_call.get)
+    b, f = wk[dom]
+    if wl.decode or dom in ("quantize", "dq_scales"):
+        ach = b / per_call[dom] / 1e6
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom}
+    else:
+        ach = f / per_call[dom] / 1e9
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_BF16_PEAK_TFS, 4), "traffic": None, "kernel": dom}
+    if wl.decode:
+        metric = "fused NF4-dequant GEMM TFLOP/s + weight-stream GB/s (% of MI355X roofline)"
+        value, unit = step_bytes / ms_step / 1e6, "GB/s"
+    else:
+        metric = "fused NF4-dequant GEMM TFLOP/s + weight-stream GB/s (% of MI355X roofline)"
+        value, unit = step_flops / ms_step / 1e9, "TFLOP/s"
+    shapes = {"7b_attn": "7B attention projection W 4096x4096", "7b_mlp_up": "7B MLP up W 11008x4096",
+              "7b_mlp_down": "7B MLP down W 4096x11008", "65b_up": "65B up W 22016x8192",
+              "65b_attn": "65B attention W 8192x8192", "tiny": "tiny W 256x256"}
+    line = {
+        "metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{shapes.get(wl.name, wl.name)} NF4 blk64 + int8 double-quant (blk256), "
+                               f"LoRA r={wl.r} alpha={wl.alpha:g}; step = quantize+DQ, fused fwd at "
+                               f"M={','.join(map(str, wl.Ms))}, fused bwd dX at M={wl.bwd_M[0]}",
+                   "name": wl.name, "N": wl.N, "K": wl.K, "M": wl.Ms, "r": wl.r, "alpha": wl.alpha,
+                   "weight_copies_rotated": wl.C, "parallelism": "single GPU"},
+        "roofline": roof,
+        "kernels": kernels,
+        "step_bytes": step_bytes, "step_flops": step_flops,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args, wl)
+        if unit == "TFLOP/s":
+            cb = line["cpu_baseline"]
+            cb["value"] = cb["value"] * step_flops / step_bytes / 1e3
+            cb["unit"] = "TFLOP/s"
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -43,25 +43,37 @@ class NF4Weight:
         return self.packed.nbytes + self.qscale.nbytes + self.step.nbytes
 
 
-def quantize(w):
+def quantize(w, packed=None, absmax=None):
     """fp32 or bf16 weight -> (packed uint8, absmax fp32). Flat block order."""
     if w.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("weight must be float32 or bfloat16")
     _need(w, w.dtype, "w")
     numel = w.numel()
-    packed = torch.empty(numel // 2, dtype=torch.uint8, device=w.device)
-    absmax = torch.empty(numel // BLOCK, dtype=torch.float32, device=w.device)
+    if packed is None:
+        packed = torch.empty(numel // 2, dtype=torch.uint8, device=w.device)
+    if absmax is None:
+        absmax = torch.empty(numel // BLOCK, dtype=torch.float32, device=w.device)
+    _need(packed, torch.uint8, "packed")
+    _need(absmax, torch.float32, "absmax")
+    if packed.numel() != numel // 2 or absmax.numel() != numel // BLOCK:
+        raise ValueError("output buffers have the wrong size")
     wdt = _lib.F32 if w.dtype == torch.float32 else _lib.BF16
     _lib.check("qlora_nf4_quantize", _lib.lib().qlora_nf4_quantize(
         _ptr(w), wdt, numel, _ptr(packed), _ptr(absmax), _stream(w.device)))
     return packed, absmax
 
 
-def dq_scales(absmax):
+def dq_scales(absmax, q=None, step=None):
     _need(absmax, torch.float32, "absmax")
     nb = absmax.numel()
-    q = torch.empty(nb, dtype=torch.int8, device=absmax.device)
-    step = torch.empty((nb + DQ_GROUP - 1) // DQ_GROUP, dtype=torch.float32, device=absmax.device)
+    if q is None:
+        q = torch.empty(nb, dtype=torch.int8, device=absmax.device)
+    if step is None:
+        step = torch.empty((nb + DQ_GROUP - 1) // DQ_GROUP, dtype=torch.float32, device=absmax.device)
+    _need(q, torch.int8, "qscale")
+    _need(step, torch.float32, "step")
+    if q.numel() != nb or step.numel() != (nb + DQ_GROUP - 1) // DQ_GROUP:
+        raise ValueError("output buffers have the wrong size")
     _lib.check("qlora_dq_scales", _lib.lib().qlora_dq_scales(
         _ptr(absmax), nb, _ptr(q), _ptr(step), _stream(absmax.device)))
     return q, step
