@@ -4,7 +4,8 @@
 Default workload: the 7B-shaped attention projection W [4096, 4096] with
 NF4 + double quantization, LoRA r=16 (alpha 32), decode shapes. One step is
 one pass of the whole hot path over one batch of synthetic input:
-  quantize W (fp32 -> NF4 codes + block absmax) -> double-quantize constants
+  quantize W (fp32 -> NF4 codes + block absmax) and double-quantize the
+  constants (one fused kernel)
   -> fused dequant forward at M = 1, 4 and 16 (each: LoRA down-projection +
      dequant-GEMV with the LoRA epilogue)
   -> fused dequant backward dX at M = 16.
@@ -15,7 +16,7 @@ the matmuls on copy c + C/2, which was written long before.
 
 value = algorithmic bytes of the step / step time (GB/s); the algorithmic
 bytes are what the method must read and write once: fp32 W read + stored
-format written for the quantize, and per matmul the stored weight
+format (0.515869 bytes/param) written for the quantize, and per matmul the stored weight
 (0.515869 bytes/param), the adapters and the activations in and out.
 
 Other shapes (--config 7b_mlp_up, 65b_up, ...) run the MFMA-bound training
@@ -119,13 +120,10 @@ class Workload:
         qw_dst = self.qw[c]
 
         def quant():
-            wl.ops.quantize(self.w[c], packed=qw_dst.packed, absmax=self.absmax_c)
+            wl.ops.quantize_dq(self.w[c], packed=qw_dst.packed, absmax=self.absmax_c, q=qw_dst.qscale,
+                               step=qw_dst.step)
 
-        def dq():
-            wl.ops.dq_scales(self.absmax_c, q=qw_dst.qscale, step=qw_dst.step)
-
-        out.append(("quantize", quant))
-        out.append(("dq_scales", dq))
+        out.append(("quantize_dq", quant))
         for M in self.Ms:
             out.append((f"fwd_M{M}", lambda M=M: wl.ops.lora_fwd(self.x[M], self.qw[u], self.A, self.B,
                                                                    self.alpha, out=self.y[M], ws=self.ws)))
@@ -137,8 +135,7 @@ class Workload:
     def work(self):
         """{label: (bytes, flops)} algorithmic work per call."""
         N, K, r = self.N, self.K, self.r
-        wk = {"quantize": (N * K * (4 + 0.5 + 4 / 64), 0.0),
-              "dq_scales": (N * K * (4 / 64 + 1 / 64) + 4 * N * K / 16384, 0.0)}
+        wk = {"quantize_dq": (quantize_bytes(N, K), 0.0)}
         for M in self.Ms:
             wk[f"fwd_M{M}"] = (matmul_bytes(M, N, K, r, 0), matmul_flops(M, N, K, r))
         for M in self.bwd_M:
@@ -278,7 +275,7 @@ def main():
             kernels[lab]["TFLOP/s"] = round(f / ms / 1e9, 2)
     dom = max(per_call, key=per_call.get)
     b, f = wk[dom]
-    if wl.decode or dom in ("quantize", "dq_scales"):
+    if wl.decode or dom == "quantize_dq":
         ach = b / per_call[dom] / 1e6
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom}

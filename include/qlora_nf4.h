@@ -101,6 +101,17 @@ int qlora_dq_scales(const float* absmax, int64_t nblocks, int8_t* qscale,
                     float* step, void* stream);
 
 /*
+ * Quantize and double-quantize in one pass: the outputs of
+ * qlora_nf4_quantize followed by qlora_dq_scales (bit-identical), from a
+ * single kernel that handles one group of 256 blocks per workgroup.
+ *   qscale [numel/64] int8 out, step [ceil(numel/16384)] fp32 out; the other
+ *   arguments as in qlora_nf4_quantize.
+ */
+int qlora_nf4_quantize_dq(const void* w, int wdt, int64_t numel, uint8_t* packed,
+                          float* absmax, int8_t* qscale, float* step,
+                          void* stream);
+
+/*
  * Standalone dequantization to bf16 (figure 2 of "A 65B fine-tune on the GPU
  * you already have"): out[i] = bf16_rne(L[code_i] * fp32(q_b * d_g)).
  *   packed [numel/2], qscale [numel/64], step [ceil(numel/16384)],

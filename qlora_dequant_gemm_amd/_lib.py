@@ -19,6 +19,7 @@ F32, BF16 = 0, 1
 _vp, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = [
     ("qlora_nf4_quantize", _i32, [_vp, _i32, _i64, _vp, _vp, _vp]),
+    ("qlora_nf4_quantize_dq", _i32, [_vp, _i32, _i64, _vp, _vp, _vp, _vp, _vp]),
     ("qlora_dq_scales", _i32, [_vp, _i64, _vp, _vp, _vp]),
     ("qlora_nf4_dequant", _i32, [_vp, _vp, _vp, _i64, _vp, _vp]),
     ("qlora_workspace_bytes", _sz, [_i32, _i64, _i64, _i64, _i32]),

@@ -88,7 +88,18 @@ int qlora_nf4_quantize(const void* w, int wdt, int64_t numel, uint8_t* packed, f
   if (!aligned16(w) || !aligned16(packed)) return QLORA_ERR_ALIGN;
   const qnf4::Codebook* cb = qnf4::codebook();
   if (!cb) return QLORA_ERR_INIT;
-  return hip_status(qnf4::launch_quantize(w, wdt, numel, packed, absmax, *cb, as_stream(stream)));
+  return hip_status(qnf4::launch_quantize(w, wdt, numel, packed, absmax, nullptr, nullptr, *cb, as_stream(stream)));
+}
+
+int qlora_nf4_quantize_dq(const void* w, int wdt, int64_t numel, uint8_t* packed, float* absmax, int8_t* qscale,
+                          float* step, void* stream) {
+  if (!w || !packed || !absmax || !qscale || !step) return QLORA_ERR_NULL;
+  if (wdt != QLORA_F32 && wdt != QLORA_BF16) return QLORA_ERR_DTYPE;
+  if (numel <= 0 || numel % QLORA_BLOCK != 0) return QLORA_ERR_SHAPE;
+  if (!aligned16(w) || !aligned16(packed)) return QLORA_ERR_ALIGN;
+  const qnf4::Codebook* cb = qnf4::codebook();
+  if (!cb) return QLORA_ERR_INIT;
+  return hip_status(qnf4::launch_quantize(w, wdt, numel, packed, absmax, qscale, step, *cb, as_stream(stream)));
 }
 
 int qlora_dq_scales(const float* absmax, int64_t nblocks, int8_t* qscale, float* step, void* stream) {

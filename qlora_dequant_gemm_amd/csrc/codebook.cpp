@@ -72,6 +72,16 @@ void derive() {
   g_cb.pad = 0.0f;
   bool ok = g_cb.L[0] == -1.0f && g_cb.L[15] == 1.0f;
   for (int j = 0; j < 15; ++j) ok = ok && g_cb.L[j] < g_cb.L[j + 1] && g_cb.T[j] >= g_cb.L[j] && g_cb.T[j] < g_cb.L[j + 1];
+  // The quantize kernel's cell lookup (cell(v) = floor(64 v + 64.5)) needs
+  // every threshold well inside its cell and at most one threshold per cell.
+  int prev_cell = -1;
+  for (int j = 0; j < 15; ++j) {
+    const double pos = static_cast<double>(g_cb.T[j]) * 64.0 + 64.5;
+    const double frac = pos - std::floor(pos);
+    const int cell = static_cast<int>(std::floor(pos));
+    ok = ok && frac > 64.0 * kCellMargin && frac < 1.0 - 64.0 * kCellMargin && cell > prev_cell;
+    prev_cell = cell;
+  }
   g_ok = ok;
 }
 

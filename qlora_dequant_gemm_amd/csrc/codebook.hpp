@@ -10,6 +10,10 @@ struct Codebook {
   float pad;
 };
 
+// Smallest distance (in normalised-weight units) required between a threshold
+// and an edge of the quantize kernel's lookup cells.
+constexpr double kCellMargin = 1e-4;
+
 // Derived once (thread-safe); nullptr if the derivation failed its checks.
 const Codebook* codebook();
 

@@ -11,9 +11,9 @@
 //   k_gemv_fwd    M <= 16: 16 weight rows per workgroup, 8 waves splitting K;
 //                 each lane dequantizes one 64-block straight into the MFMA
 //                 B-operand registers (no LDS); HBM-bound.
-//   k_gemm_fwd    M > 16: 256x256 output tile, 4 waves of 128x128, 64-deep
-//                 K steps double-buffered in LDS; one thread per weight row
-//                 dequantizes a whole 64-block into the LDS B tile; 32x32x16
+//   k_gemm_fwd    M > 16: 256x256 output tile, 4 waves each owning 64 output
+//                 columns; each lane dequantizes its MFMA B operands straight
+//                 into registers, x goes through double-buffered LDS; 32x32x16
 //                 bf16 MFMA with fp32 accumulation; LoRA as a rank-r MFMA in
 //                 the epilogue. MFMA-bound.
 //   k_gemm_bwd    M > 16: same tiling over dX [M, K]; the contraction runs over
@@ -24,186 +24,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "device.hpp"
-#include "kernels.hpp"
+#include "mm_common.hpp"
 
 namespace qnf4 {
-
-typedef __attribute__((address_space(3))) short lds_short;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-
-__device__ __forceinline__ uint16_t bf16_bits(float v) {
-  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
-}
-
-// 8 bf16 of `row` starting at col0, zero past len; one 16-byte load when the
-// whole run is in range and rows are 16-byte aligned.
-__device__ __forceinline__ u32x4 load_row8(const uint16_t* row, int64_t col0, int64_t len, bool vec_ok) {
-  if (vec_ok && col0 + 8 <= len) return ld16(row + col0);
-  uint32_t v[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int64_t c = col0 + e;
-    const uint32_t b = (c < len) ? static_cast<uint32_t>(row[c]) : 0u;
-    v[e >> 1] |= b << (16 * (e & 1));
-  }
-  return u32x4{v[0], v[1], v[2], v[3]};
-}
-
-__device__ __forceinline__ int64_t imin(int64_t a, int64_t b) { return a < b ? a : b; }
-
-// ---------------------------------------------------------------------------
-// k_lora_down: out[m][j] = sum_k in[m][k] * W(j, k),  j < rp (rows j >= r are 0)
-//   WROW:  W(j,k) = W[j*Kc + k]  (A of the forward, [r][K])
-//   !WROW: W(j,k) = W[k*r + j]   (B of the backward, [N][r])
-// Grid (ceil(M/64), S): 4 waves of 16 rows; blockIdx.y takes a K-slice.
-// PARTIAL: fp32 partial sums [S][M][rp]; else bf16 [M][rp] (S must be 1).
-// ---------------------------------------------------------------------------
-template <bool WROW, bool PARTIAL>
-__global__ __launch_bounds__(256) void k_lora_down(const uint16_t* __restrict__ in, int64_t M, int64_t Kc,
-                                                   const uint16_t* __restrict__ W, int r, int rp, int S,
-                                                   void* __restrict__ out) {
-  __shared__ u32x4 wl[128 * 8];              // [j][8 chunks] of one 64-deep K chunk
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * 64 + w * 16;
-  const int s = blockIdx.y;
-  const int64_t nch = cdiv(Kc, 64);           // the last chunk may be partial
-  const int64_t c_beg = s * nch / S, c_end = (s + 1) * nch / S;
-  const int ntile = rp / 16;
-  const int64_t arow = imin(m0 + (lane & 15), M - 1);
-  const uint16_t* in_row = in + arow * Kc;
-  f32x4 acc[8];
-#pragma unroll
-  for (int jt = 0; jt < 8; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int64_t c = c_beg; c < c_end; ++c) {
-    const int64_t k0 = c * 64;
-    if (WROW) {
-      for (int q = t; q < rp * 8; q += 256) {
-        const int j = q >> 3, ch = q & 7;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (j < r && k0 + ch * 8 < Kc) v = ld16(W + static_cast<int64_t>(j) * Kc + k0 + ch * 8);
-        wl[j * 8 + (ch ^ (j & 7))] = v;
-      }
-    } else {
-      uint16_t* wl16 = reinterpret_cast<uint16_t*>(wl);
-      for (int q = t; q < rp * 64; q += 256) {
-        const int kk = q / rp, j = q - kk * rp;
-        const uint16_t v = (j < r && k0 + kk < Kc) ? W[(k0 + kk) * r + j] : static_cast<uint16_t>(0);
-        wl16[(j * 8 + ((kk >> 3) ^ (j & 7))) * 8 + (kk & 7)] = v;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const int64_t ka = k0 + 32 * kh + 8 * (lane >> 4);   // Kc is a multiple of 8
-      const bf16x8 a = as_bf16x8(ka < Kc ? ld16(in_row + ka) : u32x4{0u, 0u, 0u, 0u});
-#pragma unroll
-      for (int jt = 0; jt < 8; ++jt) {
-        if (jt < ntile) {
-          const int j = 16 * jt + (lane & 15);
-          const bf16x8 b = as_bf16x8(wl[j * 8 + ((4 * kh + (lane >> 4)) ^ (j & 7))]);
-          acc[jt] = mfma16(a, b, acc[jt]);
-        }
-      }
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int jt = 0; jt < 8; ++jt) {
-    if (jt >= ntile) break;
-    const int j = 16 * jt + (lane & 15);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t m = m0 + 4 * (lane >> 4) + v;
-      if (m < M) {
-        if (PARTIAL)
-          static_cast<float*>(out)[(s * M + m) * rp + j] = acc[jt][v];
-        else
-          static_cast<uint16_t*>(out)[m * rp + j] = bf16_bits(acc[jt][v]);
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// k_gemv_fwd (M <= 16). Workgroup = 16 weight rows x all of K, 8 waves.
-// Lane l: g = l/16 picks one of the 4 blocks of a 256-deep super-step, c = l%16
-// is both the weight row (B operand column) and the x row (A operand row).
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(512) void k_gemv_fwd(const uint16_t* __restrict__ x, int64_t M, int64_t N,
-                                                  int64_t K, const uint8_t* __restrict__ packed,
-                                                  const int8_t* __restrict__ qscale,
-                                                  const float* __restrict__ step,
-                                                  const float* __restrict__ tpart, int St, int rp,
-                                                  const uint16_t* __restrict__ Bl, int r, float scale,
-                                                  uint16_t* __restrict__ y, Codebook cb) {
-  __shared__ f32x4 red[8][64];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int g = lane >> 4, c = lane & 15;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
-  const int64_t n = imin(n0 + c, N - 1);
-  const int64_t m = imin(static_cast<int64_t>(c), M - 1);
-  const int64_t nbr = K / 64;
-  const int64_t nss = cdiv(nbr, 4);
-  const uint8_t* prow = packed + n * (K / 2);
-  const uint16_t* xrow = x + m * K;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t ss = w; ss < nss; ss += 8) {
-    const int64_t kb = ss * 4 + g;
-    const bool valid = kb < nbr;
-    const int64_t kbc = valid ? kb : nbr - 1;
-    const u32x4 p0 = ld16(prow + kbc * 32);
-    const u32x4 p1 = ld16(prow + kbc * 32 + 16);
-    const int64_t blk = n * nbr + kbc;
-    const float sc = valid ? block_scale(qscale[blk], step[blk >> 8]) : 0.0f;
-    const uint16_t* xk = xrow + kbc * 64;
-    u32x4 xa[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) xa[j] = ld16(xk + 8 * j);
-    const MagTable tb = make_table(cb, sc);
-    const uint32_t pw[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc = mfma16(as_bf16x8(xa[j]), as_bf16x8(decode8(pw[j], tb)), acc);
-  }
-  red[w][lane] = acc;
-  __syncthreads();
-  if (w != 0) return;
-  acc = red[0][lane];
-#pragma unroll
-  for (int i = 1; i < 8; ++i) acc += red[i][lane];
-
-  if (r > 0) {
-    f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
-    const uint16_t* brow = Bl + n * r;
-    for (int js = 0; js < rp / 32; ++js) {
-      const int j0 = 32 * js + 8 * g;
-      float tv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) tv[e] = 0.f;
-      for (int s = 0; s < St; ++s) {
-        const float* tp = tpart + (s * M + m) * rp + j0;
-        const f32x4 u0 = *reinterpret_cast<const f32x4*>(tp);
-        const f32x4 u1 = *reinterpret_cast<const f32x4*>(tp + 4);
-        tv[0] += u0.x; tv[1] += u0.y; tv[2] += u0.z; tv[3] += u0.w;
-        tv[4] += u1.x; tv[5] += u1.y; tv[6] += u1.z; tv[7] += u1.w;
-      }
-      const u32x4 a = {pack_bf16x2(tv[0], tv[1]), pack_bf16x2(tv[2], tv[3]), pack_bf16x2(tv[4], tv[5]),
-                       pack_bf16x2(tv[6], tv[7])};
-      const u32x4 b = load_row8(brow, j0, r, (r & 7) == 0);
-      tmp = mfma16(as_bf16x8(a), as_bf16x8(b), tmp);
-    }
-    acc += scale * tmp;
-  }
-  const int64_t nn = n0 + c;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int64_t mm = 4 * g + v;
-    if (mm < M && nn < N) y[mm * N + nn] = bf16_bits(acc[v]);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Tiled MFMA GEMMs (M > 16)
@@ -233,6 +56,41 @@ __device__ __forceinline__ void tile_of(int pid, int ntm, int ntn, int& tm, int&
 // same logical chunk hit 8 different bank groups.
 __device__ __forceinline__ int a_slot(int row, int ch) { return row * 8 + (ch ^ (row & 7)); }
 
+// ---------------------------------------------------------------------------
+// k_gemm_fwd: y [M, N] = x . W'^T (+ LoRA), M > 16.
+//
+// Workgroup tile 256 (M) x 256 (N), 4 waves; wave w owns output columns
+// [64w, 64w + 64) for all 256 rows: 8 x 2 blocks of 32x32x16 bf16 MFMA with
+// fp32 accumulators. In this NT layout one packed dword (8 codes of one
+// weight row) is exactly one MFMA B operand, so each lane dequantizes its own
+// B operands straight into registers: no LDS for the weights and every weight
+// decoded once. x goes global -> LDS directly (global_load_lds_dwordx4: lane i
+// of a wave lands at LDS base + 16 i, so the bank swizzle is applied on the
+// global side), double-buffered.
+//
+// Per 64-deep K step k: packed codes of step k+2 are loaded into registers,
+// the MFMAs of step k run while the codes of step k+1 are decoded, and after
+// the barrier that ends the step the x tile of step k+2 is requested. Every
+// load thus has a whole step to land, and the loop (unrolled by two) keeps its
+// register sets fixed.
+//
+// K permutation: within a step, lane half h holds k in [32h, 32h + 32) and
+// MFMA sub-step s uses k = 32h + 8s + (0..7) on both operands (the sum over k
+// is order-free), so a lane's codes for a step are one 16-byte load.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
+
+struct BPacked {
+  u32x4 p[2];      // packed codes of this lane's weight row, N-block j
+  float d[2];
+  int8_t q[2];
+};
+
+// s_waitcnt vmcnt(0) (expcnt/lgkmcnt untouched), as the builtin so the
+// compiler's own wait insertion knows every earlier load has completed
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __global__ __launch_bounds__(256, 1) void k_gemm_fwd(const uint16_t* __restrict__ x, int64_t M, int64_t N,
                                                      int64_t K, const uint8_t* __restrict__ packed,
                                                      const int8_t* __restrict__ qscale,
@@ -240,96 +98,145 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd(const uint16_t* __restrict_
                                                      const uint16_t* __restrict__ tl, int rp,
                                                      const uint16_t* __restrict__ Bl, int r, float scale,
                                                      uint16_t* __restrict__ y, Codebook cb) {
-  __shared__ u32x4 smem[4 * kChunks];        // A[2], B[2]: 128 KB
-  u32x4* As = smem;
-  u32x4* Bs = smem + 2 * kChunks;
+  __shared__ u32x4 As0[kChunks];             // two distinct 32 KB buffers, so the
+  __shared__ u32x4 As1[kChunks];             // compiler can tell a DMA into one from reads of the other
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int wm = w >> 1, wn = w & 1;
   const int h = lane >> 5, l32 = lane & 31;
   const int ntm = static_cast<int>(cdiv(M, kTile)), ntn = static_cast<int>(cdiv(N, kTile));
   int tm, tn;
   tile_of(blockIdx.x, ntm, ntn, tm, tn);
   const int64_t m0 = static_cast<int64_t>(tm) * kTile, n0 = static_cast<int64_t>(tn) * kTile;
-  const int64_t nbr = K / 64;
+  const int64_t nk = K / 64;
 
-  // global -> register staging assignments
-  const int ach = t & 7, arow0 = t >> 3;
+  // x tile DMA: instruction i of wave w fills LDS rows 64w + 8i + (lane >> 3),
+  // physical chunk lane & 7, i.e. logical chunk (lane & 7) ^ (lane >> 3)
+  const int dchunk = (lane & 7) ^ (lane >> 3);
   const uint16_t* aptr[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) aptr[i] = x + imin(m0 + arow0 + 32 * i, M - 1) * K + ach * 8;
-  const int64_t brow = imin(n0 + t, N - 1);
-  const uint8_t* bptr = packed + brow * (K / 2);
-  const int64_t bblk = brow * nbr;
-
-  u32x4 areg[8];
-  u32x4 b0, b1;
-  int8_t qv;
-  float dv;
-  auto gload = [&](int64_t kt) {
+  for (int i = 0; i < 8; ++i) aptr[i] = x + imin(m0 + 64 * w + 8 * i + (lane >> 3), M - 1) * K + 8 * dchunk;
+  auto dma_a = [&](int64_t kt, u32x4* Ab) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) areg[i] = ld16(aptr[i] + kt * 64);
-    b0 = ld16(bptr + kt * 32);
-    b1 = ld16(bptr + kt * 32 + 16);
-    qv = qscale[bblk + kt];
-    dv = step[(bblk + kt) >> 8];
+    for (int i = 0; i < 8; ++i) {
+      lds_void* dst = (lds_void*)(&Ab[(64 * w + 8 * i) * 8]);
+      __builtin_amdgcn_global_load_lds((gbl_void*)(aptr[i] + kt * 64), dst, 16, 0, 0);
+    }
   };
-  auto lstore = [&](int buf) {
-    u32x4* Ab = As + buf * kChunks;
-    u32x4* Bb = Bs + buf * kChunks;
+  const uint8_t* bptr[2];
+  int64_t bblk[2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) Ab[a_slot(arow0 + 32 * i, ach)] = areg[i];
-    const MagTable tb = make_table(cb, block_scale(qv, dv));
-    const uint32_t pw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+  for (int j = 0; j < 2; ++j) {
+    const int64_t n = imin(n0 + 64 * w + 32 * j + l32, N - 1);
+    bptr[j] = packed + n * (K / 2) + 16 * h;
+    bblk[j] = n * nk;
+  }
+  auto load_b = [&](int64_t kt, BPacked& P) {
 #pragma unroll
-    for (int ch = 0; ch < 8; ++ch) Bb[a_slot(t, ch)] = decode8(pw[ch], tb);
+    for (int j = 0; j < 2; ++j) {
+      P.p[j] = ld16(bptr[j] + kt * 32);
+      P.q[j] = qscale[bblk[j] + kt];
+      P.d[j] = step[(bblk[j] + kt) >> 8];
+    }
   };
-
-  f32x16 acc[4][4];
+  f32x16 acc[8][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  auto compute = [&](int buf) {
-    const u32x4* Ab = As + buf * kChunks;
-    const u32x4* Bb = Bs + buf * kChunks;
+  // MFMAs of one step (A buffer `buf`, decoded B `bo`) with the decode of the
+  // next step's codes `nx` into `bn` spread over the four sub-steps.
+  auto step_k = [&](const u32x4* Ab, u32x4* An, const bf16x8 (&bo)[2][4], const BPacked& nx,
+                    bf16x8 (&bn)[2][4], int64_t kload, BPacked& ld, int64_t kdma) {
+    dma_a(kdma, An);
+    load_b(kload, ld);
+    __builtin_amdgcn_sched_barrier(0);         // keep this step's loads at its head
+    MagTable tb[2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int sw = (2 * ks + h) ^ (l32 & 7);
-      bf16x8 af[4], bfr[4];
+    for (int j = 0; j < 2; ++j) tb[j] = make_table(cb, block_scale(nx.q[j], nx.d[j]));
+    // A fragments double-buffered across sub-steps: those of s+1 are read
+    // while the MFMAs of s issue
+    bf16x8 afr[2][8];
+    auto read_frags = [&](int s, bf16x8 (&af)[8]) {
+      const int sw = (4 * h + s) ^ (l32 & 7);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = as_bf16x8(Ab[(128 * wm + 32 * i + l32) * 8 + sw]);
+      for (int i = 0; i < 8; ++i) af[i] = as_bf16x8(Ab[(32 * i + l32) * 8 + sw]);
+    };
+    read_frags(0, afr[0]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[j] = as_bf16x8(Bb[(128 * wn + 32 * j + l32) * 8 + sw]);
+    for (int s = 0; s < 4; ++s) {
+      if (s < 3) read_frags(s + 1, afr[(s + 1) & 1]);
+      const bf16x8 (&af)[8] = afr[s & 1];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bo[j][s], acc[i][j]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t pw = s == 0 ? nx.p[j].x : s == 1 ? nx.p[j].y : s == 2 ? nx.p[j].z : nx.p[j].w;
+        bn[j][s] = as_bf16x8(decode8(pw, tb[j]));
+      }
+    }
+    // issue order after the loads: the A fragments of sub-step 0, then each
+    // MFMA followed by four VALU ops (the decode of the next step) and, every
+    // other MFMA, one LDS read of the next sub-step's A fragments
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int m = 0; m < 64; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if ((m & 1) == 0 && m < 48) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+  };
+  auto decode_all = [&](const BPacked& P, bf16x8 (&bo)[2][4]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const MagTable tb = make_table(cb, block_scale(P.q[j], P.d[j]));
+      bo[j][0] = as_bf16x8(decode8(P.p[j].x, tb));
+      bo[j][1] = as_bf16x8(decode8(P.p[j].y, tb));
+      bo[j][2] = as_bf16x8(decode8(P.p[j].z, tb));
+      bo[j][3] = as_bf16x8(decode8(P.p[j].w, tb));
     }
   };
 
-  gload(0);
-  lstore(0);
+  BPacked P0, P1;
+  bf16x8 B0[2][4], B1[2][4];
+  dma_a(0, As0);
+  load_b(0, P0);
+  load_b(imin(1, nk - 1), P1);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vm0();
+  // pin step 1's codes here: left alone, the (read-only) loads get sunk into
+  // the loop entry, and the loop head would then drain every later load
+  asm volatile("" ::"v"(P1.p[0]), "v"(P1.p[1]), "v"(static_cast<int>(P1.q[0])), "v"(static_cast<int>(P1.q[1])),
+               "v"(P1.d[0]), "v"(P1.d[1]));
+  decode_all(P0, B0);
   __syncthreads();
-  for (int64_t kt = 0; kt < nbr; ++kt) {
-    const int cur = static_cast<int>(kt & 1);
-    const bool more = kt + 1 < nbr;
-    if (more) gload(kt + 1);
-    compute(cur);
-    if (more) lstore(cur ^ 1);
+  int64_t kt = 0;
+  // step kt reads A buffer kt%2 while the x tile of kt+1 streams into the
+  // other buffer (requested at the start of the step, after the barrier that
+  // ended step kt-1, which was the last reader of that buffer)
+  for (; kt + 2 <= nk; kt += 2) {
+    step_k(As0, As1, B0, P1, B1, imin(kt + 2, nk - 1), P0, imin(kt + 1, nk - 1));
+    wait_vm0();
+    __syncthreads();
+    step_k(As1, As0, B1, P0, B0, imin(kt + 3, nk - 1), P1, imin(kt + 2, nk - 1));
+    wait_vm0();
     __syncthreads();
   }
+  if (kt < nk) step_k(As0, As1, B0, P1, B1, nk - 1, P0, nk - 1);
+  wait_vm0();
 
+  // epilogue: LoRA up-projection as a rank-r MFMA, then bf16 stores
   if (r > 0) {
     const bool vec_ok = (r & 7) == 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t mrow = imin(m0 + 128 * wm + 32 * i + l32, M - 1);
+    for (int i = 0; i < 8; ++i) {
+      const int64_t mrow = imin(m0 + 32 * i + l32, M - 1);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t nrow = imin(n0 + 128 * wn + 32 * j + l32, N - 1);
+      for (int j = 0; j < 2; ++j) {
+        const int64_t nrow = imin(n0 + 64 * w + 32 * j + l32, N - 1);
         f32x16 tmp;
 #pragma unroll
         for (int v = 0; v < 16; ++v) tmp[v] = 0.f;
@@ -344,13 +251,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd(const uint16_t* __restrict_
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t nn = n0 + 128 * wn + 32 * j + l32;
+    for (int j = 0; j < 2; ++j) {
+      const int64_t nn = n0 + 64 * w + 32 * j + l32;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t mm = m0 + 128 * wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+        const int64_t mm = m0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
         if (mm < M && nn < N) y[mm * N + nn] = bf16_bits(acc[i][j][v]);
       }
     }
@@ -366,12 +273,6 @@ __device__ __forceinline__ int bw_slot(int row, int ch) {
   const int grp = ch >> 3;
   const int g = ((((row & 3) ^ grp) & 3) << 1) | (row & 1);
   return row * 32 + (ch ^ g);
-}
-
-__device__ __forceinline__ s16x4 ds_read_tr(const u32x4* base, int elem_off) {
-  // generic -> LDS address space (the pointer always refers to __shared__ memory)
-  lds_short* p = (lds_short*)(const_cast<short*>(reinterpret_cast<const short*>(base))) + elem_off;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
 }
 
 __global__ __launch_bounds__(256, 1) void k_gemm_bwd(const uint16_t* __restrict__ dy, int64_t M, int64_t N,
@@ -520,112 +421,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Small-M backward: grid (K/64 column tiles, S row slices). 256 weight rows per
-// step are dequantized (one 64-block each) into LDS; 4 waves each contract 64
-// of them with 16x16x32 MFMAs (B read transposed). fp32 partials [S][M][K].
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int sm_slot(int row, int ch) {
-  const int g = ((row & 3) << 1) | ((row >> 2) & 1);
-  return row * 8 + (ch ^ g);
-}
-
-__global__ __launch_bounds__(256) void k_bwd_small(const uint16_t* __restrict__ dy, int64_t M, int64_t N,
-                                                   int64_t K, const uint8_t* __restrict__ packed,
-                                                   const int8_t* __restrict__ qscale,
-                                                   const float* __restrict__ step, int S,
-                                                   float* __restrict__ part, Codebook cb) {
-  __shared__ u32x4 Bs[256 * 8];
-  __shared__ f32x4 red[4][4][64];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int64_t kt = blockIdx.x;             // 64-column tile == block column kt
-  const int s = blockIdx.y;
-  const int64_t nbr = K / 64;
-  const int64_t nsteps = cdiv(N, 256);
-  const int64_t st_beg = s * nsteps / S, st_end = (s + 1) * nsteps / S;
-  const int64_t m = imin(static_cast<int64_t>(lane & 15), M - 1);
-  const int G = lane >> 4, j16 = lane & 15;
-  f32x4 acc[4];
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int64_t st = st_beg; st < st_end; ++st) {
-    {
-      const int64_t row = imin(st * 256 + t, N - 1);
-      const uint8_t* p = packed + row * (K / 2) + kt * 32;
-      const u32x4 b0 = ld16(p), b1 = ld16(p + 16);
-      const int64_t blk = row * nbr + kt;
-      const MagTable tb = make_table(cb, block_scale(qscale[blk], step[blk >> 8]));
-      const uint32_t pw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-      for (int ch = 0; ch < 8; ++ch) Bs[sm_slot(t, ch)] = decode8(pw[ch], tb);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int64_t ncol = st * 256 + 64 * w + 32 * ks + 8 * G;
-      const u32x4 av = ncol < N ? ld16(dy + m * N + ncol) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int cbk = 0; cbk < 4; ++cbk) {
-        const int col = 16 * cbk + 4 * (j16 & 3);
-        s16x4 v[2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int row = 64 * w + 32 * ks + 8 * G + 4 * q + (j16 >> 2);
-          v[q] = ds_read_tr(Bs, sm_slot(row, col >> 3) * 8 + (col & 4));
-        }
-        const bf16x8 b = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[cbk] = mfma16(as_bf16x8(av), b, acc[cbk]);
-      }
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int cbk = 0; cbk < 4; ++cbk) red[w][cbk][lane] = acc[cbk];
-  __syncthreads();
-  {
-    const int cbk = t >> 6, ln = t & 63;
-    f32x4 sum = red[0][cbk][ln];
-#pragma unroll
-    for (int i = 1; i < 4; ++i) sum += red[i][cbk][ln];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t mm = 4 * (ln >> 4) + v;
-      if (mm < M) part[(s * M + mm) * K + kt * 64 + 16 * cbk + (ln & 15)] = sum[v];
-    }
-  }
-}
-
-// dX[m][k] = bf16( sum_s part[s][m][k] + scale * sum_j u[m][j] A[j][k] ),
-// u = bf16(sum of the down-projection partials). Grid (ceil(K/256), M).
-__global__ __launch_bounds__(256) void k_bwd_finish(const float* __restrict__ part, int S, int64_t M, int64_t K,
-                                                    const float* __restrict__ upart, int Su, int rp,
-                                                    const uint16_t* __restrict__ Al, int r, float scale,
-                                                    uint16_t* __restrict__ dx) {
-  __shared__ float us[128];
-  const int t = threadIdx.x;
-  const int64_t m = blockIdx.y;
-  const int64_t k = static_cast<int64_t>(blockIdx.x) * 256 + t;
-  if (r > 0) {
-    if (t < rp) {
-      float u = 0.f;
-      for (int s = 0; s < Su; ++s) u += upart[(s * M + m) * rp + t];
-      us[t] = bf16_lo(static_cast<uint32_t>(bf16_bits(u)));
-    }
-    __syncthreads();
-  }
-  if (k >= K) return;
-  float v = 0.f;
-  for (int s = 0; s < S; ++s) v += part[(s * M + m) * K + k];
-  if (r > 0) {
-    float l = 0.f;
-    for (int j = 0; j < r; ++j) l += us[j] * bf16_lo(static_cast<uint32_t>(Al[static_cast<int64_t>(j) * K + k]));
-    v += scale * l;
-  }
-  dx[m * K + k] = bf16_bits(v);
-}
-
-// ---------------------------------------------------------------------------
-// launchers
+// dispatch: LoRA down-projection, then the small-M or the tiled kernel
 // ---------------------------------------------------------------------------
 hipError_t launch_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
                            const int8_t* qscale, const float* step, const uint16_t* A, const uint16_t* B,
@@ -635,23 +431,17 @@ hipError_t launch_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K, c
   char* wsb = static_cast<char*>(ws);
   const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
   const int rp = r > 0 ? static_cast<int>(rank_pad(r)) : 0;
-  if (M <= kSmallM) {
-    const int St = static_cast<int>(lora_splits(M, K));
-    float* tpart = r > 0 ? reinterpret_cast<float*>(wsb + L.lora_off) : nullptr;
-    if (r > 0)
-      hipLaunchKernelGGL((k_lora_down<true, true>), dim3(static_cast<unsigned>(cdiv(M, 64)), St), dim3(256), 0,
-                         stream, x, M, K, A, r, rp, St, static_cast<void*>(tpart));
-    hipLaunchKernelGGL(k_gemv_fwd, dim3(static_cast<unsigned>(cdiv(N, 16))), dim3(512), 0, stream, x, M, N, K,
-                       packed, qscale, step, tpart, St, rp, B, r, scale, y, cb);
-  } else {
-    uint16_t* tl = r > 0 ? reinterpret_cast<uint16_t*>(wsb + L.lora_off) : nullptr;
-    if (r > 0)
-      hipLaunchKernelGGL((k_lora_down<true, false>), dim3(static_cast<unsigned>(cdiv(M, 64)), 1), dim3(256), 0,
-                         stream, x, M, K, A, r, rp, 1, static_cast<void*>(tl));
-    const int64_t tiles = cdiv(M, kTile) * cdiv(N, kTile);
-    hipLaunchKernelGGL(k_gemm_fwd, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, x, M, N, K, packed,
-                       qscale, step, tl, rp, B, r, scale, y, cb);
+  void* lora = r > 0 ? static_cast<void*>(wsb + L.lora_off) : nullptr;
+  if (r > 0) {
+    const hipError_t e = launch_lora_down(true, x, M, K, A, r, lora, stream);
+    if (e != hipSuccess) return e;
   }
+  if (M <= kSmallM)
+    return launch_fwd_small(x, M, N, K, packed, qscale, step, static_cast<const float*>(lora),
+                            static_cast<int>(lora_splits(M, K)), rp, B, r, scale, y, cb, stream);
+  const int64_t tiles = cdiv(M, kTile) * cdiv(N, kTile);
+  hipLaunchKernelGGL(k_gemm_fwd, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, x, M, N, K, packed,
+                     qscale, step, static_cast<const uint16_t*>(lora), rp, B, r, scale, y, cb);
   return hipGetLastError();
 }
 
@@ -663,27 +453,18 @@ hipError_t launch_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K, co
   char* wsb = static_cast<char*>(ws);
   const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
   const int rp = r > 0 ? static_cast<int>(rank_pad(r)) : 0;
-  if (M <= kSmallM) {
-    const int Su = static_cast<int>(lora_splits(M, N));
-    float* upart = r > 0 ? reinterpret_cast<float*>(wsb + L.lora_off) : nullptr;
-    if (r > 0)
-      hipLaunchKernelGGL((k_lora_down<false, true>), dim3(static_cast<unsigned>(cdiv(M, 64)), Su), dim3(256), 0,
-                         stream, dy, M, N, B, r, rp, Su, static_cast<void*>(upart));
-    const int Sb = static_cast<int>(bwd_small_splits(N, K));
-    float* part = reinterpret_cast<float*>(wsb + L.part_off);
-    hipLaunchKernelGGL(k_bwd_small, dim3(static_cast<unsigned>(K / 64), Sb), dim3(256), 0, stream, dy, M, N, K,
-                       packed, qscale, step, Sb, part, cb);
-    hipLaunchKernelGGL(k_bwd_finish, dim3(static_cast<unsigned>(cdiv(K, 256)), static_cast<unsigned>(M)),
-                       dim3(256), 0, stream, part, Sb, M, K, upart, Su, rp, A, r, scale, dx);
-  } else {
-    uint16_t* ul = r > 0 ? reinterpret_cast<uint16_t*>(wsb + L.lora_off) : nullptr;
-    if (r > 0)
-      hipLaunchKernelGGL((k_lora_down<false, false>), dim3(static_cast<unsigned>(cdiv(M, 64)), 1), dim3(256), 0,
-                         stream, dy, M, N, B, r, rp, 1, static_cast<void*>(ul));
-    const int64_t tiles = cdiv(M, kTile) * cdiv(K, kTile);
-    hipLaunchKernelGGL(k_gemm_bwd, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, dy, M, N, K, packed,
-                       qscale, step, ul, rp, A, r, scale, dx, cb);
+  void* lora = r > 0 ? static_cast<void*>(wsb + L.lora_off) : nullptr;
+  if (r > 0) {
+    const hipError_t e = launch_lora_down(false, dy, M, N, B, r, lora, stream);
+    if (e != hipSuccess) return e;
   }
+  if (M <= kSmallM)
+    return launch_bwd_small(dy, M, N, K, packed, qscale, step, static_cast<const float*>(lora),
+                            static_cast<int>(lora_splits(M, N)), rp, A, r, scale,
+                            reinterpret_cast<float*>(wsb + L.part_off), dx, cb, stream);
+  const int64_t tiles = cdiv(M, kTile) * cdiv(K, kTile);
+  hipLaunchKernelGGL(k_gemm_bwd, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, dy, M, N, K, packed,
+                     qscale, step, static_cast<const uint16_t*>(lora), rp, A, r, scale, dx, cb);
   return hipGetLastError();
 }
 

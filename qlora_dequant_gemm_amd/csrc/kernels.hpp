@@ -29,11 +29,12 @@ inline int64_t lora_splits(int64_t M, int64_t Kc) {
   return s < 16 ? (s < 1 ? 1 : s) : 16;
 }
 
-// Row slices of the small-M backward (fp32 partials of dX).
+// Row slices of the small-M backward (fp32 partials of dX): enough column
+// tiles x slices for about one workgroup per CU, 1024 weight rows per step.
 inline int64_t bwd_small_splits(int64_t N, int64_t K) {
   const int64_t ktiles = cdiv(K, 64);
   int64_t s = cdiv(256, ktiles);
-  const int64_t steps = cdiv(N, 256);
+  const int64_t steps = cdiv(N, 1024);
   if (s > steps) s = steps;
   if (s < 1) s = 1;
   return s;
@@ -63,12 +64,27 @@ inline WsLayout ws_layout(int op, int64_t M, int64_t N, int64_t K, int r) {
   return w;
 }
 
+// qscale/step may be NULL (quantize only); otherwise the constants are also
+// double-quantized in the same pass.
 hipError_t launch_quantize(const void* w, int wdt, int64_t numel, uint8_t* packed, float* absmax,
-                           const Codebook& cb, hipStream_t stream);
+                           int8_t* qscale, float* step, const Codebook& cb, hipStream_t stream);
 hipError_t launch_dq_scales(const float* absmax, int64_t nblocks, int8_t* qscale, float* step,
                             hipStream_t stream);
 hipError_t launch_dequant(const uint8_t* packed, const int8_t* qscale, const float* step, int64_t numel,
                           uint16_t* out, const Codebook& cb, hipStream_t stream);
+
+// rank-r down projection of `in` [M][Kc] by the adapter (wrow: A [r][Kc];
+// else B [Kc][r]); M <= kSmallM writes lora_splits fp32 partials, else bf16.
+hipError_t launch_lora_down(bool wrow, const uint16_t* in, int64_t M, int64_t Kc, const uint16_t* W, int r,
+                            void* out, hipStream_t stream);
+hipError_t launch_fwd_small(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
+                            const int8_t* qscale, const float* step, const float* tpart, int St, int rp,
+                            const uint16_t* B, int r, float scale, uint16_t* y, const Codebook& cb,
+                            hipStream_t stream);
+hipError_t launch_bwd_small(const uint16_t* dy, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
+                            const int8_t* qscale, const float* step, const float* upart, int Su, int rp,
+                            const uint16_t* A, int r, float scale, float* part, uint16_t* dx,
+                            const Codebook& cb, hipStream_t stream);
 
 hipError_t launch_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
                            const int8_t* qscale, const float* step, const uint16_t* A, const uint16_t* B,

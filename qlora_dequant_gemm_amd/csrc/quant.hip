@@ -1,9 +1,11 @@
 // Quantize, double-quantize and dequantize kernels for gfx950.
 //
-//  k_quantize  -- block absmax with a 16-lane reduction, fp32 normalisation,
-//                 nearest-level code by binary search on the thresholds,
-//                 nibble packing. ("A 65B fine-tune on the GPU you already
-//                 have", figures 3 and 4.)
+//  k_quantize  -- one workgroup per group of 256 blocks: block absmax with a
+//                 16-lane DPP reduction, nearest-level code (cell lookup with
+//                 an exact fallback near thresholds), nibble packing, and
+//                 optionally the double quantization of the group's
+//                 constants. ("A 65B fine-tune on the GPU you already have",
+//                 figures 3 and 4.)
 //  k_dq_scales -- one workgroup per group of 256 block constants: group max,
 //                 step = max / 127, int8 codes. (same page, figure 4.)
 //  k_dequant   -- packed codes + int8 scales + fp32 steps -> bf16, with the
@@ -20,27 +22,77 @@
 namespace qnf4 {
 
 // ---------------------------------------------------------------------------
-// k_quantize: 16 lanes per 64-weight block, 4 consecutive weights per lane.
+// Nearest-code selection.
+//
+// Exact rule: v = fp32(w / absmax) (IEEE division), code = #{j : v > T_j}.
+// Fast path: v' = w * rcp(absmax) is within 2.4e-7 of v. The line is cut
+// into 129 cells, cell(v) = floor(64 v + 64.5); cell edges are at least
+// 1.2e-3 away from every threshold (checked when the codebook is derived),
+// so each cell holds at most one threshold and
+//     code(v') = base[cell] + (v' > thr[cell])
+// with base[cell] the thresholds in lower cells. code(v') == code(v) unless a
+// threshold lies between v and v', which puts v' within 1e-6 of thr[cell];
+// those (rare) elements take the exact rule.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t nearest_code(float v, const Codebook& cb) {
+constexpr int kCells = 129;
+
+struct CellEntry {
+  float thr;      // the threshold inside this cell, or +inf
+  int base;       // thresholds in lower cells
+};
+
+// v in [-1 - 1e-6, 1 + 1e-6] maps to [0.49, 128.51], so truncation is the
+// floor and the index is always a valid cell.
+__device__ __forceinline__ int cell_of(float v) { return static_cast<int>(fmaf(v, 64.0f, 64.5f)); }
+
+__device__ __forceinline__ uint32_t search_code(float v, const Codebook& cb) {
   // number of thresholds strictly below v, by binary search over T[0..14]
   uint32_t c = (v > cb.T[7]) ? 8u : 0u;
   float t = (c & 8u) ? cb.T[11] : cb.T[3];
   c += (v > t) ? 4u : 0u;
-  float t2a = (c & 4u) ? cb.T[13] : cb.T[9];
-  float t2b = (c & 4u) ? cb.T[5] : cb.T[1];
+  const float t2a = (c & 4u) ? cb.T[13] : cb.T[9];
+  const float t2b = (c & 4u) ? cb.T[5] : cb.T[1];
   t = (c & 8u) ? t2a : t2b;
   c += (v > t) ? 2u : 0u;
-  // c in {0,2,...,14}: compare with T[c]
-  float e0 = (c & 2u) ? cb.T[2] : cb.T[0];
-  float e1 = (c & 2u) ? cb.T[6] : cb.T[4];
-  float e2 = (c & 2u) ? cb.T[10] : cb.T[8];
-  float e3 = (c & 2u) ? cb.T[14] : cb.T[12];
-  float f0 = (c & 4u) ? e1 : e0;
-  float f1 = (c & 4u) ? e3 : e2;
+  const float e0 = (c & 2u) ? cb.T[2] : cb.T[0];
+  const float e1 = (c & 2u) ? cb.T[6] : cb.T[4];
+  const float e2 = (c & 2u) ? cb.T[10] : cb.T[8];
+  const float e3 = (c & 2u) ? cb.T[14] : cb.T[12];
+  const float f0 = (c & 4u) ? e1 : e0;
+  const float f1 = (c & 4u) ? e3 : e2;
   t = (c & 8u) ? f1 : f0;
   c += (v > t) ? 1u : 0u;
   return c;
+}
+
+__device__ __forceinline__ uint32_t exact_code(float w, float a, const Codebook& cb) {
+  const float v = (a == 0.0f) ? 0.0f : w / a;      // IEEE division
+  return search_code(v, cb);
+}
+
+__device__ void build_lut(CellEntry* lut, const Codebook& cb) {
+  for (int i = threadIdx.x; i < kCells; i += blockDim.x) {
+    int base = 0;
+    float thr = __builtin_inff();
+#pragma unroll
+    for (int j = 0; j < 15; ++j) {
+      const int cj = cell_of(cb.T[j]);
+      base += cj < i ? 1 : 0;
+      if (cj == i) thr = cb.T[j];
+    }
+    lut[i] = CellEntry{thr, base};
+  }
+}
+
+// max over the 16 lanes of a row (DPP row rotations, then quad permutes) of
+// non-negative floats, compared as their bit patterns (same order)
+__device__ __forceinline__ float row16_max_nonneg(float a) {
+  uint32_t x = __builtin_bit_cast(uint32_t, a);
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(x), static_cast<int>(x), 0x128, 0xF, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(x), static_cast<int>(x), 0x124, 0xF, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(x), static_cast<int>(x), 0xB1, 0xF, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(x), static_cast<int>(x), 0x4E, 0xF, 0xF, false)));
+  return __builtin_bit_cast(float, x);
 }
 
 template <typename Tin>
@@ -62,34 +114,100 @@ struct Load4<uint16_t> {
   }
 };
 
-template <typename Tin>
+// ---------------------------------------------------------------------------
+// k_quantize: one 256-thread workgroup per group of 256 blocks (16384
+// weights). 16 rounds of 16 blocks, 16 lanes per block and 4 consecutive
+// weights per lane; all 16 rounds of loads are issued before any is used.
+// With DQ the group's constants are double-quantized in the same pass.
+// ---------------------------------------------------------------------------
+template <typename Tin, bool DQ>
 __global__ __launch_bounds__(256) void k_quantize(const Tin* __restrict__ w, int64_t nblocks,
                                                   uint16_t* __restrict__ packed16,
-                                                  float* __restrict__ absmax, Codebook cb) {
-  const int lane16 = threadIdx.x & 15;
-  const int64_t first = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 4;
-  const int64_t stride = (static_cast<int64_t>(gridDim.x) * blockDim.x) >> 4;
-  for (int64_t b = first; b < nblocks; b += stride) {
-    const f32x4 v = Load4<Tin>::at(w + b * 64 + lane16 * 4);
-    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    // max over the 16 lanes of this block (xor offsets stay inside the group)
-    a = fmaxf(a, __shfl_xor(a, 8, 16));
-    a = fmaxf(a, __shfl_xor(a, 4, 16));
-    a = fmaxf(a, __shfl_xor(a, 2, 16));
-    a = fmaxf(a, __shfl_xor(a, 1, 16));
-    uint32_t c0, c1, c2, c3;
-    if (a == 0.0f) {
-      c0 = c1 = c2 = c3 = nearest_code(0.0f, cb);
-    } else {
-      c0 = nearest_code(v.x / a, cb);          // IEEE division (correctly rounded)
-      c1 = nearest_code(v.y / a, cb);
-      c2 = nearest_code(v.z / a, cb);
-      c3 = nearest_code(v.w / a, cb);
-    }
-    const uint32_t word = c0 | (c1 << 4) | (c2 << 8) | (c3 << 12);
-    packed16[b * 16 + lane16] = static_cast<uint16_t>(word);   // 32 bytes per block
-    if (lane16 == 0) absmax[b] = a;
+                                                  float* __restrict__ absmax, int8_t* __restrict__ qscale,
+                                                  float* __restrict__ step, Codebook cb) {
+  __shared__ CellEntry lut[kCells];
+  __shared__ float amax_s[256];
+  __shared__ float wmax[4];
+  const int t = threadIdx.x, lane16 = t & 15, sub = t >> 4;
+  const int64_t g = blockIdx.x;
+  const int64_t b0 = g * 256;
+  const int nb_here = static_cast<int>(nblocks - b0 < 256 ? nblocks - b0 : 256);
+  f32x4 v[16];
+#pragma unroll
+  for (int rd = 0; rd < 16; ++rd) {
+    const int bl = rd * 16 + sub;
+    const int64_t b = b0 + (bl < nb_here ? bl : 0);
+    v[rd] = Load4<Tin>::at(w + b * 64 + lane16 * 4);
   }
+  build_lut(lut, cb);
+  __syncthreads();
+  // fast path for all 64 elements of this thread; a round with any element
+  // near a threshold (or a zero / tiny block) is flagged and redone exactly
+  uint32_t redo = 0;
+#pragma unroll
+  for (int rd = 0; rd < 16; ++rd) {
+    const int bl = rd * 16 + sub;
+    const float a = row16_max_nonneg(fmaxf(fmaxf(fabsf(v[rd].x), fabsf(v[rd].y)),
+                                           fmaxf(fabsf(v[rd].z), fabsf(v[rd].w))));
+    const bool fast = a >= 1e-30f;               // uniform over the block's 16 lanes
+    const float ra = fast ? __builtin_amdgcn_rcpf(a) : 0.0f;
+    uint32_t word = 0;
+    bool near = !fast;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float we = e == 0 ? v[rd].x : e == 1 ? v[rd].y : e == 2 ? v[rd].z : v[rd].w;
+      const float vp = we * ra;
+      const CellEntry ce = lut[cell_of(vp)];
+      word |= (static_cast<uint32_t>(ce.base) + (vp > ce.thr ? 1u : 0u)) << (4 * e);
+      near = near || !(fabsf(vp - ce.thr) > 1e-6f);
+    }
+    redo |= near ? (1u << rd) : 0u;
+    asm volatile("" ::"v"(redo));                // keep the check in this round (register pressure)
+    if (bl < nb_here) {
+      const int64_t b = b0 + bl;
+      packed16[b * 16 + lane16] = static_cast<uint16_t>(word);
+      if (lane16 == 0) {
+        absmax[b] = a;
+        amax_s[bl] = a;
+      }
+    }
+  }
+  __syncthreads();                               // amax_s complete
+  if (redo) {                                    // rare: exact rule for the flagged rounds
+#pragma unroll 1
+    for (int rd = 0; rd < 16; ++rd) {
+      const int bl = rd * 16 + sub;
+      if (!(redo & (1u << rd)) || bl >= nb_here) continue;
+      const int64_t b = b0 + bl;
+      const f32x4 x = Load4<Tin>::at(w + b * 64 + lane16 * 4);
+      const float a = amax_s[bl];
+      uint32_t word = 0;
+#pragma unroll 1
+      for (int e = 0; e < 4; ++e) {
+        const float we = e == 0 ? x.x : e == 1 ? x.y : e == 2 ? x.z : x.w;
+        word |= exact_code(we, a, cb) << (4 * e);
+      }
+      packed16[b * 16 + lane16] = static_cast<uint16_t>(word);
+    }
+  }
+  if (!DQ) return;
+  // double quantization of this group's constants (same arithmetic as k_dq_scales)
+  const float a = t < nb_here ? amax_s[t] : 0.0f;
+  float m = a;
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if ((t & 63) == 0) wmax[t >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float d = m / 127.0f;
+  if (t < nb_here) {
+    int q = 0;
+    if (d != 0.0f) {
+      const float r = fminf(fmaxf(__builtin_rintf(a / d), -127.0f), 127.0f);
+      q = static_cast<int>(r);
+    }
+    qscale[b0 + t] = static_cast<int8_t>(q);
+  }
+  if (t == 0) step[g] = d;
 }
 
 // ---------------------------------------------------------------------------
@@ -152,15 +270,24 @@ static int grid_for(int64_t work_items, int per_block) {
 }
 
 hipError_t launch_quantize(const void* w, int wdt, int64_t numel, uint8_t* packed, float* absmax,
-                           const Codebook& cb, hipStream_t stream) {
+                           int8_t* qscale, float* step, const Codebook& cb, hipStream_t stream) {
   const int64_t nb = numel / 64;
-  const int grid = grid_for(nb, 16);           // 16 blocks per 256-thread workgroup
-  if (wdt == 0)
-    hipLaunchKernelGGL(k_quantize<float>, dim3(grid), dim3(256), 0, stream,
-                       static_cast<const float*>(w), nb, reinterpret_cast<uint16_t*>(packed), absmax, cb);
-  else
-    hipLaunchKernelGGL(k_quantize<uint16_t>, dim3(grid), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(w), nb, reinterpret_cast<uint16_t*>(packed), absmax, cb);
+  const dim3 grid(static_cast<unsigned>((nb + 255) / 256));
+  uint16_t* p16 = reinterpret_cast<uint16_t*>(packed);
+  const bool dq = qscale != nullptr;
+  if (wdt == 0) {
+    const float* wf = static_cast<const float*>(w);
+    if (dq)
+      hipLaunchKernelGGL((k_quantize<float, true>), grid, dim3(256), 0, stream, wf, nb, p16, absmax, qscale, step, cb);
+    else
+      hipLaunchKernelGGL((k_quantize<float, false>), grid, dim3(256), 0, stream, wf, nb, p16, absmax, qscale, step, cb);
+  } else {
+    const uint16_t* wb = static_cast<const uint16_t*>(w);
+    if (dq)
+      hipLaunchKernelGGL((k_quantize<uint16_t, true>), grid, dim3(256), 0, stream, wb, nb, p16, absmax, qscale, step, cb);
+    else
+      hipLaunchKernelGGL((k_quantize<uint16_t, false>), grid, dim3(256), 0, stream, wb, nb, p16, absmax, qscale, step, cb);
+  }
   return hipGetLastError();
 }
 

@@ -1,0 +1,300 @@
+// Decode-shaped (M <= 16) fused NF4-dequant matmuls for gfx950.
+//
+// At these shapes every weight is used by at most 16 rows, so the kernels are
+// bound by streaming the 0.516 bytes/param NF4 weight from HBM. They are
+// written to keep as many loads in flight as possible: operands of the next
+// step are loaded while the current one is decoded and multiplied, and the
+// epilogue's inputs are fetched at kernel start.
+//
+//   k_gemv_fwd    y = x . W'^T (+ LoRA): 16 weight rows per workgroup, 16 waves
+//                 splitting K; each lane dequantizes one 64-block straight
+//                 into 16x16x32 MFMA B-operand registers.
+//   k_bwd_small   dX partials: 64-column tiles x row slices; 1024 weight rows
+//                 per step dequantized into LDS and read transposed
+//                 (ds_read_b64_tr_b16).
+//   k_bwd_finish  dX = bf16(sum of the row-slice partials + LoRA term).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mm_common.hpp"
+
+namespace qnf4 {
+
+struct GemvStage {
+  u32x4 p0, p1;      // 32 packed bytes = one 64-block of one weight row
+  u32x4 xa[8];       // the matching 64 activations of one x row
+  float d;
+  int8_t q;
+  bool valid;
+};
+
+// ---------------------------------------------------------------------------
+// k_gemv_fwd. Lane l: g = l/16 selects one of the 4 blocks of a 256-deep
+// super-step, c = l%16 is the weight row (B column) and the x row (A row).
+// Dynamic LDS: rp/32 * kGemvWaves * 64 * 32 bytes for the LoRA t sums.
+// ---------------------------------------------------------------------------
+constexpr int kGemvWaves = 16;
+
+__global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_fwd(const uint16_t* __restrict__ x, int64_t M, int64_t N,
+                                                  int64_t K, const uint8_t* __restrict__ packed,
+                                                  const int8_t* __restrict__ qscale,
+                                                  const float* __restrict__ step,
+                                                  const float* __restrict__ tpart, int St, int rp,
+                                                  const uint16_t* __restrict__ Bl, int r, float scale,
+                                                  uint16_t* __restrict__ y, Codebook cb) {
+  __shared__ f32x4 red[kGemvWaves][64];
+  extern __shared__ f32x4 tred[];            // [wave][js][lane][2]
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int64_t n = imin(n0 + c, N - 1);
+  const int64_t m = imin(static_cast<int64_t>(c), M - 1);
+  const int64_t nbr = K / 64;
+  const int64_t nss = cdiv(nbr, 4);
+  const uint8_t* prow = packed + n * (K / 2);
+  const uint16_t* xrow = x + m * K;
+  const int njs = r > 0 ? rp / 32 : 0;
+
+  // epilogue operands first (ranks up to 64; larger ranks load the rest after
+  // the main loop): this wave's share of the t partial sums, and (wave 0) the
+  // B rows of the LoRA up-projection
+  constexpr int kPre = 2;
+  f32x4 tv[4][2];
+  u32x4 bop[4];
+#pragma unroll
+  for (int js = 0; js < 4; ++js) {
+    tv[js][0] = tv[js][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bop[js] = u32x4{0u, 0u, 0u, 0u};
+  }
+  const uint16_t* brow = Bl + n * r;
+  auto load_epi = [&](int js) {
+    for (int s = w; s < St; s += kGemvWaves) {
+      const float* tp = tpart + (s * M + m) * rp + 32 * js + 8 * g;
+      tv[js][0] += *reinterpret_cast<const f32x4*>(tp);
+      tv[js][1] += *reinterpret_cast<const f32x4*>(tp + 4);
+    }
+    if (w == 0) bop[js] = load_row8(brow, 32 * js + 8 * g, r, (r & 7) == 0);
+  };
+#pragma unroll
+  for (int js = 0; js < kPre; ++js)
+    if (js < njs) load_epi(js);
+
+  auto load_stage = [&](int64_t ss, GemvStage& st) {
+    const int64_t kb = ss * 4 + g;
+    st.valid = kb < nbr;
+    const int64_t kbc = st.valid ? kb : nbr - 1;
+    st.p0 = ld16(prow + kbc * 32);
+    st.p1 = ld16(prow + kbc * 32 + 16);
+    const int64_t blk = n * nbr + kbc;
+    st.q = qscale[blk];
+    st.d = step[blk >> 8];
+    const uint16_t* xk = xrow + kbc * 64;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st.xa[j] = ld16(xk + 8 * j);
+  };
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto run_stage = [&](const GemvStage& st) {
+    const float sc = st.valid ? block_scale(st.q, st.d) : 0.0f;
+    const MagTable tb = make_table(cb, sc);
+    const uint32_t pw[8] = {st.p0.x, st.p0.y, st.p0.z, st.p0.w, st.p1.x, st.p1.y, st.p1.z, st.p1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = mfma16(as_bf16x8(st.xa[j]), as_bf16x8(decode8(pw[j], tb)), acc);
+  };
+  // one super-step per iteration (loads carried across iterations would make
+  // the compiler wait on all of them at the loop head); for K up to 4096
+  // every wave has a single super-step
+  for (int64_t ss = w; ss < nss; ss += kGemvWaves) {
+    GemvStage st;
+    load_stage(ss, st);
+    run_stage(st);
+  }
+
+#pragma unroll
+  for (int js = kPre; js < 4; ++js)
+    if (js < njs) load_epi(js);
+  red[w][lane] = acc;
+#pragma unroll
+  for (int js = 0; js < 4; ++js) {
+    if (js < njs) {
+      tred[((w * njs + js) * 64 + lane) * 2 + 0] = tv[js][0];
+      tred[((w * njs + js) * 64 + lane) * 2 + 1] = tv[js][1];
+    }
+  }
+  __syncthreads();
+  if (w != 0) return;
+  acc = red[0][lane];
+#pragma unroll
+  for (int i = 1; i < kGemvWaves; ++i) acc += red[i][lane];
+  if (njs > 0) {
+    f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int js = 0; js < 4; ++js) {
+      if (js < njs) {
+        f32x4 s0 = tred[((0 * njs + js) * 64 + lane) * 2 + 0];
+        f32x4 s1 = tred[((0 * njs + js) * 64 + lane) * 2 + 1];
+#pragma unroll
+        for (int i = 1; i < kGemvWaves; ++i) {
+          s0 += tred[((i * njs + js) * 64 + lane) * 2 + 0];
+          s1 += tred[((i * njs + js) * 64 + lane) * 2 + 1];
+        }
+        const u32x4 a = {pack_bf16x2(s0.x, s0.y), pack_bf16x2(s0.z, s0.w), pack_bf16x2(s1.x, s1.y),
+                         pack_bf16x2(s1.z, s1.w)};
+        tmp = mfma16(as_bf16x8(a), as_bf16x8(bop[js]), tmp);
+      }
+    }
+    acc += scale * tmp;
+  }
+  const int64_t nn = n0 + c;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int64_t mm = 4 * g + v;
+    if (mm < M && nn < N) y[mm * N + nn] = bf16_bits(acc[v]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_bwd_small: grid (K/64 column tiles, S row slices), 16 waves. Each step
+// dequantizes 1024 weight rows x one 64-column block (one block per thread)
+// into LDS; wave w contracts rows [64w, 64w + 64) of the step on 16x16x32
+// MFMAs with the B operand read transposed. The LDS tile is reused for the
+// cross-wave reduction.
+// ---------------------------------------------------------------------------
+constexpr int kBwdWaves = 16;
+constexpr int kBwdRows = 64 * kBwdWaves;       // weight rows per step
+
+__device__ __forceinline__ int sm_slot(int row, int ch) {
+  // 8 consecutive rows writing one chunk hit 8 bank groups; the 4 rows one
+  // transposed read touches get 4 distinct chunk pairs
+  const int sw = ((row & 3) << 1) | ((row >> 2) & 1);
+  return row * 8 + (ch ^ sw);
+}
+
+__global__ __launch_bounds__(64 * kBwdWaves) void k_bwd_small(const uint16_t* __restrict__ dy, int64_t M,
+                                                              int64_t N, int64_t K,
+                                                              const uint8_t* __restrict__ packed,
+                                                              const int8_t* __restrict__ qscale,
+                                                              const float* __restrict__ step, int S,
+                                                              float* __restrict__ part, Codebook cb) {
+  __shared__ u32x4 Bs[kBwdRows * 8];         // 128 KB: one step's tile, then the reduction
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int64_t kt = blockIdx.x;             // 64-column tile == block column kt
+  const int s = blockIdx.y;
+  const int64_t nbr = K / 64;
+  const int64_t nsteps = cdiv(N, kBwdRows);
+  const int64_t st_beg = s * nsteps / S, st_end = (s + 1) * nsteps / S;
+  const int64_t m = imin(static_cast<int64_t>(lane & 15), M - 1);
+  const int G = lane >> 4, j16 = lane & 15;
+  f32x4 acc[4];
+#pragma unroll
+  for (int cbk = 0; cbk < 4; ++cbk) acc[cbk] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int64_t st = st_beg; st < st_end; ++st) {
+    // this thread's weight row-block and this wave's dY fragments
+    const int64_t row = imin(st * kBwdRows + t, N - 1);
+    const uint8_t* p = packed + row * (K / 2) + kt * 32;
+    const u32x4 b0 = ld16(p), b1 = ld16(p + 16);
+    const int64_t blk = row * nbr + kt;
+    const int8_t qv = qscale[blk];
+    const float dv = step[blk >> 8];
+    u32x4 av[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int64_t ncol = st * kBwdRows + 64 * w + 32 * ks + 8 * G;
+      av[ks] = ncol < N ? ld16(dy + m * N + ncol) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (st > st_beg) __syncthreads();        // previous step's reads are done
+    {
+      const MagTable tb = make_table(cb, block_scale(qv, dv));
+      const uint32_t pw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+      for (int ch = 0; ch < 8; ++ch) Bs[sm_slot(t, ch)] = decode8(pw[ch], tb);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int cbk = 0; cbk < 4; ++cbk) {
+        const int col = 16 * cbk + 4 * (j16 & 3);
+        s16x4 v[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int rr = 64 * w + 32 * ks + 8 * G + 4 * q + (j16 >> 2);
+          v[q] = ds_read_tr(Bs, sm_slot(rr, col >> 3) * 8 + (col & 4));
+        }
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[cbk] = mfma16(as_bf16x8(av[ks]), bv, acc[cbk]);
+      }
+    }
+  }
+  __syncthreads();                             // tile reads done: reuse LDS
+  f32x4* red = reinterpret_cast<f32x4*>(Bs);   // [wave][cbk][lane]
+#pragma unroll
+  for (int cbk = 0; cbk < 4; ++cbk) red[(w * 4 + cbk) * 64 + lane] = acc[cbk];
+  __syncthreads();
+  if (t < 256) {
+    const int cbk = t >> 6, ln = t & 63;
+    f32x4 sum = red[cbk * 64 + ln];
+#pragma unroll
+    for (int i = 1; i < kBwdWaves; ++i) sum += red[(i * 4 + cbk) * 64 + ln];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t mm = 4 * (ln >> 4) + v;
+      if (mm < M) part[(s * M + mm) * K + kt * 64 + 16 * cbk + (ln & 15)] = sum[v];
+    }
+  }
+}
+
+// dX[m][k] = bf16( sum_s part[s][m][k] + scale * sum_j u[m][j] A[j][k] ),
+// u = bf16(sum of the down-projection partials). Grid (ceil(K/256), M).
+__global__ __launch_bounds__(256) void k_bwd_finish(const float* __restrict__ part, int S, int64_t M, int64_t K,
+                                                    const float* __restrict__ upart, int Su, int rp,
+                                                    const uint16_t* __restrict__ Al, int r, float scale,
+                                                    uint16_t* __restrict__ dx) {
+  __shared__ float us[128];
+  const int t = threadIdx.x;
+  const int64_t m = blockIdx.y;
+  const int64_t k = static_cast<int64_t>(blockIdx.x) * 256 + t;
+  const int64_t kc = imin(k, K - 1);
+  float v = 0.f;
+  for (int s = 0; s < S; ++s) v += part[(s * M + m) * K + kc];
+  if (r > 0) {
+    if (t < rp) {
+      float u = 0.f;
+      for (int s = 0; s < Su; ++s) u += upart[(s * M + m) * rp + t];
+      us[t] = bf16_lo(static_cast<uint32_t>(bf16_bits(u)));
+    }
+    __syncthreads();
+    float l = 0.f;
+#pragma unroll 8
+    for (int j = 0; j < r; ++j) l += us[j] * bf16_lo(static_cast<uint32_t>(Al[static_cast<int64_t>(j) * K + kc]));
+    v += scale * l;
+  }
+  if (k < K) dx[m * K + k] = bf16_bits(v);
+}
+
+// ---------------------------------------------------------------------------
+// launchers (M <= 16)
+// ---------------------------------------------------------------------------
+hipError_t launch_fwd_small(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
+                            const int8_t* qscale, const float* step, const float* tpart, int St, int rp,
+                            const uint16_t* B, int r, float scale, uint16_t* y, const Codebook& cb,
+                            hipStream_t stream) {
+  const size_t lds = r > 0 ? static_cast<size_t>(rp / 32) * kGemvWaves * 64 * 32 : 0;
+  hipLaunchKernelGGL(k_gemv_fwd, dim3(static_cast<unsigned>(cdiv(N, 16))), dim3(64 * kGemvWaves), lds, stream, x, M,
+                     N, K,
+                     packed, qscale, step, tpart, St, rp, B, r, scale, y, cb);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_small(const uint16_t* dy, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
+                            const int8_t* qscale, const float* step, const float* upart, int Su, int rp,
+                            const uint16_t* A, int r, float scale, float* part, uint16_t* dx,
+                            const Codebook& cb, hipStream_t stream) {
+  const int S = static_cast<int>(bwd_small_splits(N, K));
+  hipLaunchKernelGGL(k_bwd_small, dim3(static_cast<unsigned>(K / 64), S), dim3(64 * kBwdWaves), 0, stream, dy, M,
+                     N, K, packed, qscale, step, S, part, cb);
+  hipLaunchKernelGGL(k_bwd_finish, dim3(static_cast<unsigned>(cdiv(K, 256)), static_cast<unsigned>(M)), dim3(256),
+                     0, stream, part, S, M, K, upart, Su, rp, A, r, scale, dx);
+  return hipGetLastError();
+}
+
+}  // namespace qnf4

@@ -79,10 +79,33 @@ def dq_scales(absmax, q=None, step=None):
     return q, step
 
 
+def quantize_dq(w, packed=None, absmax=None, q=None, step=None):
+    """Quantize + double-quantize in one kernel: (packed, absmax, qscale, step)."""
+    if w.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("weight must be float32 or bfloat16")
+    _need(w, w.dtype, "w")
+    numel = w.numel()
+    nb = numel // BLOCK
+    ng = (nb + DQ_GROUP - 1) // DQ_GROUP
+    dev = w.device
+    packed = torch.empty(numel // 2, dtype=torch.uint8, device=dev) if packed is None else packed
+    absmax = torch.empty(nb, dtype=torch.float32, device=dev) if absmax is None else absmax
+    q = torch.empty(nb, dtype=torch.int8, device=dev) if q is None else q
+    step = torch.empty(ng, dtype=torch.float32, device=dev) if step is None else step
+    for t, dt, n, name in [(packed, torch.uint8, numel // 2, "packed"), (absmax, torch.float32, nb, "absmax"),
+                           (q, torch.int8, nb, "qscale"), (step, torch.float32, ng, "step")]:
+        _need(t, dt, name)
+        if t.numel() != n:
+            raise ValueError(f"{name} has the wrong size")
+    wdt = _lib.F32 if w.dtype == torch.float32 else _lib.BF16
+    _lib.check("qlora_nf4_quantize_dq", _lib.lib().qlora_nf4_quantize_dq(
+        _ptr(w), wdt, numel, _ptr(packed), _ptr(absmax), _ptr(q), _ptr(step), _stream(dev)))
+    return packed, absmax, q, step
+
+
 def quantize_weight(w):
     """Full storage format of a 2-D weight [N, K]: NF4 codes + double-quantized constants."""
-    packed, absmax = quantize(w)
-    q, step = dq_scales(absmax)
+    packed, _, q, step = quantize_dq(w)
     return NF4Weight(packed, q, step, w.shape)
 
 

@@ -118,3 +118,15 @@ def test_quantize_dq_dequant_reject_bad_arguments():
     assert L.qlora_nf4_dequant(FAKE, V(0), FAKE, 64, FAKE, V(0)) == 1
     a = (ctypes.c_float * 16)()
     assert L.qlora_nf4_codebook(a, None) == 1
+
+
+def test_thresholds_sit_well_inside_quantize_cells():
+    """The quantize kernel looks codes up in 129 cells of width 1/64 (cell =
+    floor(64 v + 64.5)) and re-derives a code exactly only within 1e-6 of the
+    cell's threshold; that is exact if every threshold is far from a cell edge
+    and no two share a cell."""
+    _, thresholds = ops.codebook()
+    pos = np.array(thresholds, np.float64) * 64 + 64.5
+    frac = pos - np.floor(pos)
+    assert np.min(np.minimum(frac, 1 - frac)) / 64 > 1e-4
+    assert len(set(np.floor(pos).astype(int))) == 15

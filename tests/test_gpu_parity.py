@@ -96,6 +96,60 @@ def test_exact_level_weights_code_to_themselves(qops):
     assert np.array_equal(nf4.unpack(packed.cpu().numpy()), c.astype(np.uint8))
 
 
+def _near_threshold_weights():
+    """Blocks whose absmax is 1, so w / absmax = w exactly: every threshold,
+    its fp32 neighbours and the levels themselves, in both signs."""
+    L = nf4.codebook().astype(np.float64)
+    vals = []
+    for j in range(15):
+        m = np.float32((L[j] + L[j + 1]) / 2)
+        x = m
+        for _ in range(3):
+            x = np.nextafter(x, np.float32(-2))
+        for _ in range(7):
+            vals.append(x)
+            x = np.nextafter(x, np.float32(2))
+    vals += list(nf4.codebook()) + [np.float32(0.0), np.float32(-0.0), np.float32(1e-9), np.float32(-1e-9)]
+    vals = np.array(vals, np.float32)
+    n = 63 * ((vals.size + 62) // 63)
+    vals = np.resize(vals, n).reshape(-1, 63)
+    w = np.concatenate([np.ones((vals.shape[0], 1), np.float32), vals], axis=1)   # absmax 1 per block
+    # the same pattern scaled by a power of two (division still exact) and by 0.37 (inexact)
+    return np.concatenate([w.reshape(-1), (w * np.float32(0.125)).reshape(-1),
+                           (w * np.float32(0.37)).reshape(-1)]).astype(np.float32)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_quantize_near_thresholds_bit_exact(qops, fused):
+    w = _near_threshold_weights()
+    w = np.concatenate([w, np.zeros(64 * 300 - w.size % (64 * 300), np.float32)]) if w.size % 64 else w
+    if fused:
+        packed, absmax, q, step = qops.quantize_dq(dev(w))
+    else:
+        packed, absmax = qops.quantize(dev(w))
+        q, step = qops.dq_scales(absmax)
+    opk, oa = nf4.quantize(w)
+    oq, ostep = nf4.double_quantize(oa)
+    assert np.array_equal(packed.cpu().numpy(), opk)
+    assert np.array_equal(q.cpu().numpy(), oq)
+    assert np.array_equal(step.cpu().numpy().view(np.uint32), ostep.view(np.uint32))
+
+
+@pytest.mark.parametrize("N,K,bf16", [(300, 320, False), (1000, 1024, True), (3, 64, False)])
+def test_fused_quantize_dq_equals_separate(qops, N, K, bf16):
+    w = synth.weight(N, K, 70 + N)
+    if bf16:
+        w = synth.to_bf16_bits(w)
+    wt = dev(w)
+    p1, a1 = qops.quantize(wt)
+    q1, s1 = qops.dq_scales(a1)
+    p2, a2, q2, s2 = qops.quantize_dq(wt)
+    for x1, x2 in [(p1, p2), (a1, a2), (q1, q2), (s1, s2)]:
+        assert torch.equal(x1, x2)
+    opk, oq, ostep, _ = nf4.quantize_all(w)
+    assert np.array_equal(p2.cpu().numpy(), opk) and np.array_equal(q2.cpu().numpy(), oq)
+
+
 @pytest.mark.parametrize("name", ["7b_attn", "7b_mlp_up"])
 def test_quantize_full_size_bit_exact(qops, name):
     c = synth.CONFIGS[name]
