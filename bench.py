@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--copies", type=int, default=0, help="weight copies rotated (0 = auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle CPU time")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                   help="only run a plain device-to-device copy of BYTES bytes 3 times (the reference "
+                        "kernel that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return p.parse_args()
 
 
@@ -144,7 +147,7 @@ class Workload:
 
 
 def run_gpu(args):
-    """Step time from graph replays; per-call kernel times from an eager pass."""
+    """Step time and per-call times, both from graph replays timed with events."""
     import torch
     wl = Workload(args.config, args.copies)
     labels = [lab for lab, _ in wl.calls(0)]
@@ -182,20 +185,27 @@ def run_gpu(args):
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(end) / args.steps
 
-    # per-call durations: a GPU-side sleep lets the host enqueue a whole step
-    # before the GPU starts it, so the events bracket kernel execution only
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(labels) + 1)] for _ in range(args.steps)]
-    with torch.cuda.stream(stream):
-        for s in range(args.steps):
-            calls = wl.calls(args.warmup + s)
-            torch.cuda._sleep(2_000_000)
-            ev[s][0].record(stream)
-            for i, (_, fn) in enumerate(calls):
-                fn()
-                ev[s][i + 1].record(stream)
-    torch.cuda.synchronize()
-    per_call = {lab: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
-                for i, lab in enumerate(labels)}
+    # per-call durations: for each call, one graph runs it once per weight copy
+    # of the rotation (C launches back to back, each on a different copy);
+    # events on the launch stream bracket `reps` replays of that graph
+    per_call = {}
+    reps = max(2, args.steps // wl.C)
+    for i, lab in enumerate(labels):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for c in range(wl.C):
+                wl.calls(c)[i][1]()
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        per_call[lab] = e0.elapsed_time(e1) / (reps * wl.C)
     return wl, ms_step, per_call, wall
 
 
@@ -214,18 +224,21 @@ def cpu_baseline(args, wl):
     c = synth.CONFIGS[wl.name]
     s = c["seeds"]
     N, K, r, alpha = wl.N, wl.K, wl.r, wl.alpha
-    # sample: whole rows of W (a row-slice is a valid smaller instance of the
-    # same per-row work), sized to about --cpu-seconds of oracle time
+    # sample: slices of whole rows of W (a row slice is a smaller instance of
+    # the same per-row work: quantize + DQ + dequant of those rows and the
+    # matmuls against them), taken in turn until about --cpu-seconds of oracle
+    # time has been spent; the rate is scaled to the step's algorithmic bytes
     w = synth.weight(N, K, s["w"], c.get("outliers", 0.0), s.get("outliers"))
     A, B = synth.adapters(N, K, r, s["A"], s["B"])
-    rows = min(N, 256)
     xs = {M: synth.activations(M, K, s["x"]) for M in wl.Ms}
     dys = {M: synth.activations(M, N, s["dy"]) for M in wl.bwd_M}
-    total_bytes = 0.0
+    step_bytes = sum(b for b, _ in wl.work().values())
+    rows = min(N, 256)                      # multiple of 4: 1024 weights = whole DQ groups
+    done_rows = 0
     t_total = 0.0
-    reps = 0
-    while True:
-        n0 = (reps * rows) % N
+    passes = 0
+    while t_total < args.cpu_seconds and t_total < 120.0:
+        n0 = (passes * rows) % N
         sl = slice(n0, min(N, n0 + rows))
         ws = w[sl]
         nrow = ws.shape[0]
@@ -237,19 +250,79 @@ def cpu_baseline(args, wl):
         for M in wl.bwd_M:
             gemm.backward_dx(dys[M][:, sl], wd, A, B[sl], alpha, r)
         t_total += time.perf_counter() - t
-        frac = nrow / N
-        wk = wl.work()
-        total_bytes += frac * sum(b for b, _ in wk.values())
-        reps += 1
-        if t_total >= args.cpu_seconds or reps * rows >= 4 * N:
-            break
-        if t_total < args.cpu_seconds / 8 and rows < N:
-            rows = min(N, rows * 2)
+        done_rows += nrow
+        passes += 1
+    total_bytes = step_bytes * done_rows / N
     return {"value": total_bytes / t_total / 1e9, "unit": "GB/s", "cores": int(max(1, blas_threads)),
             "host_cores": cores, "kind": "oracle",
-            "sample": f"{reps} oracle passes over row slices of W ({rows} rows each of {N}x{K}; "
-                      f"quantize+DQ+dequant single-threaded numpy, fp64 matmuls on {blas_threads} BLAS "
-                      f"threads); {t_total:.1f} s of CPU time, scaled to the same algorithmic bytes"}
+            "sample": f"{passes} oracle passes over {rows}-row slices of W {N}x{K} ({done_rows} rows = "
+                      f"{done_rows / N:.3f} of one step): quantize + double-quant + dequant (numpy, one "
+                      f"thread) and the fp64 forward at M={','.join(map(str, wl.Ms))} and backward dX at "
+                      f"M={wl.bwd_M[0]} ({blas_threads} BLAS threads); {t_total:.1f} s, scaled to the "
+                      f"step's algorithmic bytes"}
+
+
+# ---------------------------------------------------------------------------
+# HBM traffic of the dominant kernel, from committed counter summaries
+# ---------------------------------------------------------------------------
+CSRC = os.path.join(ROOT, "qlora_dequant_gemm_amd", "csrc")
+# call label -> (kernel, translation unit that defines it)
+CALL_KERNEL = {"quantize_dq": ("k_quantize", "quant.hip"), "fwd": ("k_gemv_fwd", "small.hip"),
+               "fwd_big": ("k_gemm_fwd", "gemm.hip"), "bwd": ("k_bwd_small", "small.hip"),
+               "bwd_big": ("k_gemm_bwd", "gemm.hip")}
+
+
+def kernel_of(label, M):
+    key = label.split("_M")[0]
+    if key in ("fwd", "bwd") and M > 16:
+        key += "_big"
+    return CALL_KERNEL[key]
+
+
+def source_digest(unit):
+    """sha256 over a translation unit and every local header it includes."""
+    import hashlib
+    import re
+    seen, todo = [], [unit]
+    while todo:
+        f = todo.pop()
+        if f in seen:
+            continue
+        seen.append(f)
+        text = open(os.path.join(CSRC, f)).read()
+        todo += [g for g in re.findall(r'#include "([^"]+)"', text) if os.path.exists(os.path.join(CSRC, g))]
+    h = hashlib.sha256()
+    for f in sorted(seen):
+        h.update(f.encode())
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel, unit, config):
+    """Bytes per launch from profiles/<kernel>_<config>_traffic.txt, or None when
+    there is no such summary or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{config}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_digest") != source_digest(unit):
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def copy_probe(nbytes):
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": a.numel() * 4}), flush=True)
 
 
 def main():
@@ -262,6 +335,9 @@ def main():
     if not torch.cuda.is_available():
         sys.stderr.write("bench.py needs a GPU\n")
         sys.exit(1)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     wl, ms_step, per_call, wall = run_gpu(args)
     wk = wl.work()
     step_bytes = sum(b for b, _ in wk.values())
@@ -275,14 +351,18 @@ def main():
             kernels[lab]["TFLOP/s"] = round(f / ms / 1e9, 2)
     dom = max(per_call, key=per_call.get)
     b, f = wk[dom]
+    kname, unit_src = kernel_of(dom, max(wl.Ms))
+    traffic = read_traffic(kname, unit_src, wl.name)
     if wl.decode or dom == "quantize_dq":
         ach = b / per_call[dom] / 1e6
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom}
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kname, "call": dom,
+                "algorithmic_bytes": b, "ms": round(per_call[dom], 5)}
     else:
         ach = f / per_call[dom] / 1e9
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                "frac": round(ach / MFMA_BF16_PEAK_TFS, 4), "traffic": None, "kernel": dom}
+                "frac": round(ach / MFMA_BF16_PEAK_TFS, 4), "traffic": traffic, "kernel": kname, "call": dom,
+                "algorithmic_flops": f, "ms": round(per_call[dom], 5)}
     if wl.decode:
         metric = "fused NF4-dequant GEMM TFLOP/s + weight-stream GB/s (% of MI355X roofline)"
         value, unit = step_bytes / ms_step / 1e6, "GB/s"

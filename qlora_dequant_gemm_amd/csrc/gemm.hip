@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "mm_common.hpp"
 
 namespace qnf4 {
@@ -52,9 +54,13 @@ __device__ __forceinline__ void tile_of(int pid, int ntm, int ntn, int& tm, int&
 }
 
 // A tile (256 rows x 64 deep, bf16) in LDS: row-major, 8 chunks of 16 bytes
-// per row, chunk index xor (row & 7) so that 8 consecutive rows reading the
-// same logical chunk hit 8 different bank groups.
-__device__ __forceinline__ int a_slot(int row, int ch) { return row * 8 + (ch ^ (row & 7)); }
+// per row. The LDS has 64 four-byte banks and serves a 16-byte-per-lane read
+// 16 lanes at a time; a 128-byte row covers half the banks, so rows of one
+// parity share a half. Logical chunk c of row r sits at physical chunk
+// c ^ ((r >> 1) & 7): 16 consecutive rows reading the same logical chunk then
+// land on 8 distinct chunks in each half, i.e. on all 64 banks once.
+__device__ __forceinline__ int a_swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int a_slot(int row, int ch) { return row * 8 + (ch ^ a_swz(row)); }
 
 // ---------------------------------------------------------------------------
 // k_gemm_fwd: y [M, N] = x . W'^T (+ LoRA), M > 16.
@@ -63,34 +69,59 @@ __device__ __forceinline__ int a_slot(int row, int ch) { return row * 8 + (ch ^ 
 // [64w, 64w + 64) for all 256 rows: 8 x 2 blocks of 32x32x16 bf16 MFMA with
 // fp32 accumulators. In this NT layout one packed dword (8 codes of one
 // weight row) is exactly one MFMA B operand, so each lane dequantizes its own
-// B operands straight into registers: no LDS for the weights and every weight
-// decoded once. x goes global -> LDS directly (global_load_lds_dwordx4: lane i
-// of a wave lands at LDS base + 16 i, so the bank swizzle is applied on the
-// global side), double-buffered.
+// B operands straight into registers and every weight is decoded once.
 //
-// Per 64-deep K step k: packed codes of step k+2 are loaded into registers,
-// the MFMAs of step k run while the codes of step k+1 are decoded, and after
-// the barrier that ends the step the x tile of step k+2 is requested. Every
-// load thus has a whole step to land, and the loop (unrolled by two) keeps its
-// register sets fixed.
+// Memory traffic is what limits this kernel, so every stream is moved in
+// whole 128-byte lines:
+//   x      global -> LDS by DMA (buffer_load ... lds), a ring of four 256x64
+//          tiles; the tile of step k+3 is requested at the start of step k.
+//   codes  each wave DMAs the codes of its own 64 weight rows for a super-step
+//          of four K steps (64 rows x 128 bytes = 8 KB) into a private LDS
+//          slab; lanes then read their 16-byte code words from LDS. The slab
+//          of super-step S+1 is requested in step 4S+2, right after that
+//          step has read the last codes of super-step S.
+//   scales q and d of step k+2 are loaded at the start of step k.
+// In step k the MFMAs of step k run while the codes of step k+1 are decoded.
+// LDS: 4 x 32 KB of x + 4 x 8 KB of codes = 160 KB, one workgroup per CU.
 //
 // K permutation: within a step, lane half h holds k in [32h, 32h + 32) and
 // MFMA sub-step s uses k = 32h + 8s + (0..7) on both operands (the sum over k
-// is order-free), so a lane's codes for a step are one 16-byte load.
+// is order-free), so a lane's codes for a step are one 16-byte word.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void gbl_void;
+constexpr int kBufferDword3 = 0x00020000;    // raw buffer descriptor word 3 on gfx9-family parts
 
-struct BPacked {
-  u32x4 p[2];      // packed codes of this lane's weight row, N-block j
+// Workgroup barrier without the fence of __syncthreads (whose release half
+// waits for every outstanding vector load). The asm memory clobber keeps the
+// compiler from moving memory accesses across it; the caller waits for the
+// LDS DMA it needs published, and its own LDS reads of the buffer about to be
+// refilled have all been consumed by then.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+struct BScale {
+  float d[2];      // second-level steps of this lane's weight rows (N-blocks j)
+  int8_t q[2];     // block scale codes
+  float live;      // 1 for a real K step, 0 for a step past the end
+};
+struct BScale4 {   // the same for the four steps of a super-step
   float d[2];
-  int8_t q[2];
+  uint32_t q[2];   // byte u = scale code of step 4S + u
 };
 
-// s_waitcnt vmcnt(0) (expcnt/lgkmcnt untouched), as the builtin so the
-// compiler's own wait insertion knows every earlier load has completed
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(n) with expcnt/lgkmcnt left alone (gfx9 encoding: vmcnt
+// bits 3:0 and 15:14), as the builtin so that the compiler's own wait
+// insertion knows which loads have completed
+constexpr int vmcnt_imm(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }
+template <int N>
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(N)); }
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// kQuad: K is a multiple of 256, so the four block-scale codes of a
+// super-step are one aligned 4-byte word of qscale and share one second-level
+// step (a 256-block group never splits 4-aligned blocks); scales are then
+// loaded once per super-step. Otherwise they are loaded per step.
+template <bool kQuad>
 __global__ __launch_bounds__(256, 1) void k_gemm_fwd(const uint16_t* __restrict__ x, int64_t M, int64_t N,
                                                      int64_t K, const uint8_t* __restrict__ packed,
                                                      const int8_t* __restrict__ qscale,
@@ -98,44 +129,100 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd(const uint16_t* __restrict_
                                                      const uint16_t* __restrict__ tl, int rp,
                                                      const uint16_t* __restrict__ Bl, int r, float scale,
                                                      uint16_t* __restrict__ y, Codebook cb) {
-  __shared__ u32x4 As0[kChunks];             // two distinct 32 KB buffers, so the
-  __shared__ u32x4 As1[kChunks];             // compiler can tell a DMA into one from reads of the other
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  // ring of four x tiles (32 KB each) and the per-wave code slabs (8 KB each),
+  // distinct objects so that the compiler can tell a DMA into one from reads
+  // of another
+  __shared__ u32x4 As0[kChunks];
+  __shared__ u32x4 As1[kChunks];
+  __shared__ u32x4 As2[kChunks];
+  __shared__ u32x4 As3[kChunks];
+  __shared__ u32x4 Bs[4 * 512];
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave index, provably uniform (SGPR)
   const int h = lane >> 5, l32 = lane & 31;
   const int ntm = static_cast<int>(cdiv(M, kTile)), ntn = static_cast<int>(cdiv(N, kTile));
   int tm, tn;
   tile_of(blockIdx.x, ntm, ntn, tm, tn);
+  tm = __builtin_amdgcn_readfirstlane(tm);     // uniform already; this keeps the
+  tn = __builtin_amdgcn_readfirstlane(tn);     // buffer descriptors in SGPRs
   const int64_t m0 = static_cast<int64_t>(tm) * kTile, n0 = static_cast<int64_t>(tn) * kTile;
   const int64_t nk = K / 64;
+  const int64_t nsup = (nk + 3) / 4;           // super-steps of four K steps
 
-  // x tile DMA: instruction i of wave w fills LDS rows 64w + 8i + (lane >> 3),
-  // physical chunk lane & 7, i.e. logical chunk (lane & 7) ^ (lane >> 3)
-  const int dchunk = (lane & 7) ^ (lane >> 3);
-  const uint16_t* aptr[8];
+  // x tile DMA (rows past M read as zero through the descriptor's range
+  // check). Instruction i of wave w fills LDS rows 64w + 8i + (lane >> 3),
+  // physical chunk lane & 7, i.e. logical chunk (lane & 7) ^ a_swz(row); the
+  // K step goes in soffset.
+  const int64_t rows_valid = imin(static_cast<int64_t>(kTile), M - m0);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x + m0 * K), 0, static_cast<int>(rows_valid * K * 2), kBufferDword3);
+  uint32_t voff[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) aptr[i] = x + imin(m0 + 64 * w + 8 * i + (lane >> 3), M - 1) * K + 8 * dchunk;
+  for (int i = 0; i < 8; ++i) {
+    const int row = 64 * w + 8 * i + (lane >> 3);
+    voff[i] = static_cast<uint32_t>(row * K * 2 + 16 * ((lane & 7) ^ a_swz(row)));
+  }
   auto dma_a = [&](int64_t kt, u32x4* Ab) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       lds_void* dst = (lds_void*)(&Ab[(64 * w + 8 * i) * 8]);
-      __builtin_amdgcn_global_load_lds((gbl_void*)(aptr[i] + kt * 64), dst, 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, dst, 16, voff[i], static_cast<uint32_t>(kt * 128), 0, 0);
     }
   };
-  const uint8_t* bptr[2];
+  // code slab DMA: wave w's rows n0 + 64w + r, r = 8i + (lane >> 3), bytes
+  // [128 S, 128 S + 128) of each packed row, same chunk swizzle as x. A
+  // super-step past the end re-reads the last one (its steps are dead).
+  const int64_t nrows_valid = imin(static_cast<int64_t>(kTile), N - n0);
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(packed + n0 * (K / 2)), 0, static_cast<int>(nrows_valid * (K / 2)), kBufferDword3);
+  uint32_t boff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r8 = 8 * i + (lane >> 3);
+    boff[i] = static_cast<uint32_t>((64 * w + r8) * (K / 2) + 16 * ((lane & 7) ^ a_swz(r8)));
+  }
+  u32x4* const Bw = Bs + 512 * w;              // this wave's slab: 64 rows x 8 chunks
+  auto dma_b = [&](int64_t S) {
+    const uint32_t so = static_cast<uint32_t>(imin(S, nsup - 1) * 128);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      lds_void* dst = (lds_void*)(&Bw[64 * i]);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, dst, 16, boff[i], so, 0, 0);
+    }
+  };
+  // the 16-byte code words of K step kt for this lane (N-blocks j = 0, 1)
+  auto read_codes = [&](int64_t kt, u32x4 (&c)[2]) {
+    const int ch = (2 * static_cast<int>(kt & 3) + h) ^ a_swz(l32);   // a_swz(32 j + l32) == a_swz(l32)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) c[j] = Bw[(32 * j + l32) * 8 + ch];
+  };
   int64_t bblk[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int64_t n = imin(n0 + 64 * w + 32 * j + l32, N - 1);
-    bptr[j] = packed + n * (K / 2) + 16 * h;
-    bblk[j] = n * nk;
-  }
-  auto load_b = [&](int64_t kt, BPacked& P) {
+  for (int j = 0; j < 2; ++j) bblk[j] = imin(n0 + 64 * w + 32 * j + l32, N - 1) * nk;
+  // block scales of K step kt; a step past the end (the loop runs whole
+  // super-steps) re-reads the last one and is marked dead, which makes its
+  // block scale, and so every decoded weight, zero
+  auto load_s = [&](int64_t kt, BScale& P) {
+    const int64_t kc = imin(kt, nk - 1);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      P.p[j] = ld16(bptr[j] + kt * 32);
-      P.q[j] = qscale[bblk[j] + kt];
-      P.d[j] = step[(bblk[j] + kt) >> 8];
+      P.q[j] = qscale[bblk[j] + kc];
+      P.d[j] = step[(bblk[j] + kc) >> 8];
     }
+    P.live = kt < nk ? 1.0f : 0.0f;
+  };
+  auto load_s4 = [&](int64_t S, BScale4& P) {
+    const int64_t kc = 4 * imin(S, nsup - 1);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      P.q[j] = *reinterpret_cast<const uint32_t*>(qscale + bblk[j] + kc);
+      P.d[j] = step[(bblk[j] + kc) >> 8];
+    }
+  };
+  // scales of step kt (position u in its super-step) from a quad
+  auto scale_of = [&](const BScale4& P, int u, int64_t kt, int j) {
+    const int8_t q = static_cast<int8_t>((P.q[j] >> (8 * u)) & 0xFFu);
+    return block_scale(q, P.d[j]) * (kt < nk ? 1.0f : 0.0f);
   };
   f32x16 acc[8][2];
 #pragma unroll
@@ -144,22 +231,39 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd(const uint16_t* __restrict_
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  bf16x8 B0_[2][4], B1[2][4];                  // decoded B of the current / next step
 
-  // MFMAs of one step (A buffer `buf`, decoded B `bo`) with the decode of the
-  // next step's codes `nx` into `bn` spread over the four sub-steps.
-  auto step_k = [&](const u32x4* Ab, u32x4* An, const bf16x8 (&bo)[2][4], const BPacked& nx,
-                    bf16x8 (&bn)[2][4], int64_t kload, BPacked& ld, int64_t kdma) {
-    dma_a(kdma, An);
-    load_b(kload, ld);
-    __builtin_amdgcn_sched_barrier(0);         // keep this step's loads at its head
+  // One K step k (position u = k % 4 in its super-step): reads x tile Ab,
+  // multiplies with the decoded B `bo`, decodes the codes of step k+1 (read
+  // here from the slab) with the block scales scales_next(j) into `bn`,
+  // requests x tile k+3 into An, issues this step's scale loads
+  // (issue_scales) and, at u == 2, the next super-step's code slab.
+  auto step_k = [&](auto u_c, const u32x4* Ab, u32x4* An, const bf16x8 (&bo)[2][4], bf16x8 (&bn)[2][4],
+                    auto&& issue_scales, auto&& scales_next, int64_t k) {
+    constexpr int u = decltype(u_c)::value;
+    u32x4 cw[2];
+    read_codes(k + 1, cw);
+    if constexpr (u == 2) {
+      // the slab's last reads have landed: refill it first, so that waiting
+      // for it (end of this step) leaves this step's x-tile and scale loads
+      // in flight
+      wait_lgkm0();
+      asm volatile("" ::: "memory");
+      dma_b(k / 4 + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    dma_a(imin(k + 3, nk - 1), An);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_scales();
+    __builtin_amdgcn_sched_barrier(0);
     MagTable tb[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) tb[j] = make_table(cb, block_scale(nx.q[j], nx.d[j]));
+    for (int j = 0; j < 2; ++j) tb[j] = make_table(cb, scales_next(j));
     // A fragments double-buffered across sub-steps: those of s+1 are read
     // while the MFMAs of s issue
     bf16x8 afr[2][8];
     auto read_frags = [&](int s, bf16x8 (&af)[8]) {
-      const int sw = (4 * h + s) ^ (l32 & 7);
+      const int sw = (4 * h + s) ^ a_swz(l32);     // a_swz(32 i + l32) == a_swz(l32)
 #pragma unroll
       for (int i = 0; i < 8; ++i) af[i] = as_bf16x8(Ab[(32 * i + l32) * 8 + sw]);
     };
@@ -174,7 +278,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd(const uint16_t* __restrict_
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bo[j][s], acc[i][j]);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const uint32_t pw = s == 0 ? nx.p[j].x : s == 1 ? nx.p[j].y : s == 2 ? nx.p[j].z : nx.p[j].w;
+        const uint32_t pw = s == 0 ? cw[j].x : s == 1 ? cw[j].y : s == 2 ? cw[j].z : cw[j].w;
         bn[j][s] = as_bf16x8(decode8(pw, tb[j]));
       }
     }
@@ -189,44 +293,108 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd(const uint16_t* __restrict_
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     }
   };
-  auto decode_all = [&](const BPacked& P, bf16x8 (&bo)[2][4]) {
+  using U0 = std::integral_constant<int, 0>;
+  using U1 = std::integral_constant<int, 1>;
+  using U2 = std::integral_constant<int, 2>;
+  using U3 = std::integral_constant<int, 3>;
+  auto decode_step0 = [&](auto&& scale0) {
+    u32x4 c0[2];
+    read_codes(0, c0);
+    bf16x8 (&bo)[2][4] = B0_;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const MagTable tb = make_table(cb, block_scale(P.q[j], P.d[j]));
-      bo[j][0] = as_bf16x8(decode8(P.p[j].x, tb));
-      bo[j][1] = as_bf16x8(decode8(P.p[j].y, tb));
-      bo[j][2] = as_bf16x8(decode8(P.p[j].z, tb));
-      bo[j][3] = as_bf16x8(decode8(P.p[j].w, tb));
+      const MagTable tb = make_table(cb, scale0(j));
+      bo[j][0] = as_bf16x8(decode8(c0[j].x, tb));
+      bo[j][1] = as_bf16x8(decode8(c0[j].y, tb));
+      bo[j][2] = as_bf16x8(decode8(c0[j].z, tb));
+      bo[j][3] = as_bf16x8(decode8(c0[j].w, tb));
     }
   };
+  bf16x8 (&B0)[2][4] = B0_;
+  auto nothing = [] {};
 
-  BPacked P0, P1;
-  bf16x8 B0[2][4], B1[2][4];
-  dma_a(0, As0);
-  load_b(0, P0);
-  load_b(imin(1, nk - 1), P1);
-  __builtin_amdgcn_sched_barrier(0);
-  wait_vm0();
-  // pin step 1's codes here: left alone, the (read-only) loads get sunk into
-  // the loop entry, and the loop head would then drain every later load
-  asm volatile("" ::"v"(P1.p[0]), "v"(P1.p[1]), "v"(static_cast<int>(P1.q[0])), "v"(static_cast<int>(P1.q[1])),
-               "v"(P1.d[0]), "v"(P1.d[1]));
-  decode_all(P0, B0);
-  __syncthreads();
-  int64_t kt = 0;
-  // step kt reads A buffer kt%2 while the x tile of kt+1 streams into the
-  // other buffer (requested at the start of the step, after the barrier that
-  // ended step kt-1, which was the last reader of that buffer)
-  for (; kt + 2 <= nk; kt += 2) {
-    step_k(As0, As1, B0, P1, B1, imin(kt + 2, nk - 1), P0, imin(kt + 1, nk - 1));
-    wait_vm0();
-    __syncthreads();
-    step_k(As1, As0, B1, P0, B0, imin(kt + 3, nk - 1), P1, imin(kt + 2, nk - 1));
-    wait_vm0();
-    __syncthreads();
+  // Prologue: the loads of "steps -2 and -1" in the order the loop issues
+  // them, so that the loop's wait counts hold from step 0 on.
+  // Vector-memory loads per step, in order: at u == 2 the code slab (8), then
+  // x tile k+3 (8), then the scale loads (quad path: 4 at u == 1 for the next
+  // super-step; per-step path: 4 for step k+2). The end of step k waits for x
+  // tile k+1, issued in step k-2; whatever was issued after it may stay in
+  // flight, and that count is the argument of each wait_vm below. Step u == 2
+  // waits instead for the code slab it requested first (so only its own
+  // x-tile and scale loads stay in flight): the next step reads that slab
+  // right after the barrier. These explicit waits are what order the slab
+  // DMA before its reads: the compiler's own LDS-DMA tracking cannot be
+  // relied on to cover reads at other offsets of the slab.
+  if constexpr (kQuad) {
+    BScale4 Qc, Qn;
+    load_s4(0, Qc);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_a(0, As0);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_b(0);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_a(imin(1, nk - 1), As1);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_a(imin(2, nk - 1), As2);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<16>();                             // scales of super-step 0, x tile 0, code slab 0
+    decode_step0([&](int j) { return scale_of(Qc, 0, 0, j); });
+    lds_barrier();
+    for (int64_t S = 0; S < nsup; ++S) {
+      const int64_t k = 4 * S;
+      step_k(U0{}, As0, As3, B0, B1, nothing, [&](int j) { return scale_of(Qc, 1, k + 1, j); }, k);
+      wait_vm<16>();
+      lds_barrier();
+      step_k(U1{}, As1, As0, B1, B0, [&] { load_s4(S + 1, Qn); },
+             [&](int j) { return scale_of(Qc, 2, k + 2, j); }, k + 1);
+      wait_vm<20>();
+      lds_barrier();
+      step_k(U2{}, As2, As1, B0, B1, nothing, [&](int j) { return scale_of(Qc, 3, k + 3, j); }, k + 2);
+      wait_vm<8>();                            // also the code slab requested first in this step
+      lds_barrier();
+      step_k(U3{}, As3, As2, B1, B0, nothing, [&](int j) { return scale_of(Qn, 0, k + 4, j); }, k + 3);
+      wait_vm<28>();
+      lds_barrier();
+      Qc = Qn;
+    }
+  } else {
+    BScale P0, P1;
+    dma_a(0, As0);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_b(0);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_a(imin(1, nk - 1), As1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_s(0, P0);
+    __builtin_amdgcn_sched_barrier(0);
+    dma_a(imin(2, nk - 1), As2);
+    __builtin_amdgcn_sched_barrier(0);
+    load_s(1, P1);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<12>();                             // everything up to the scales of step 0
+    // pin step 1's scales here: left alone, the (read-only) loads get sunk
+    // into the loop entry, and the loop head would then drain every later load
+    asm volatile("" ::"v"(static_cast<int>(P1.q[0])), "v"(static_cast<int>(P1.q[1])), "v"(P1.d[0]), "v"(P1.d[1]));
+    decode_step0([&](int j) { return block_scale(P0.q[j], P0.d[j]) * P0.live; });
+    lds_barrier();
+    auto sc = [](const BScale& P, int j) { return block_scale(P.q[j], P.d[j]) * P.live; };
+    for (int64_t S = 0; S < nsup; ++S) {
+      const int64_t k = 4 * S;
+      step_k(U0{}, As0, As3, B0, B1, [&] { load_s(k + 2, P0); }, [&](int j) { return sc(P1, j); }, k);
+      wait_vm<28>();
+      lds_barrier();
+      step_k(U1{}, As1, As0, B1, B0, [&] { load_s(k + 3, P1); }, [&](int j) { return sc(P0, j); }, k + 1);
+      wait_vm<28>();
+      lds_barrier();
+      step_k(U2{}, As2, As1, B0, B1, [&] { load_s(k + 4, P0); }, [&](int j) { return sc(P1, j); }, k + 2);
+      wait_vm<12>();                           // also the code slab requested first in this step
+      lds_barrier();
+      step_k(U3{}, As3, As2, B1, B0, [&] { load_s(k + 5, P1); }, [&](int j) { return sc(P0, j); }, k + 3);
+      wait_vm<36>();
+      lds_barrier();
+    }
   }
-  if (kt < nk) step_k(As0, As1, B0, P1, B1, nk - 1, P0, nk - 1);
-  wait_vm0();
+  wait_vm<0>();
 
   // epilogue: LoRA up-projection as a rank-r MFMA, then bf16 stores
   if (r > 0) {
@@ -250,17 +418,30 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd(const uint16_t* __restrict_
       }
     }
   }
+  // bf16 stores: for fixed (i, j, v) the 32 lanes of a half-wave write 64
+  // contiguous bytes of one row; interior tiles skip the bounds checks
+  if (m0 + kTile <= M && n0 + kTile <= N) {
+    uint16_t* yt = y + (m0 + 4 * h) * N + n0 + 64 * w + l32;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t nn = n0 + 64 * w + 32 * j + l32;
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t mm = m0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (mm < M && nn < N) y[mm * N + nn] = bf16_bits(acc[i][j][v]);
+        for (int v = 0; v < 16; ++v)
+          yt[(32 * i + 8 * (v >> 2) + (v & 3)) * N + 32 * j] = bf16_bits(acc[i][j][v]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t nn = n0 + 64 * w + 32 * j + l32;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t mm = m0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (mm < M && nn < N) y[mm * N + nn] = bf16_bits(acc[i][j][v]);
+        }
       }
-    }
+  }
 }
 
 // B tile of the backward: 64 weight rows x 256 output columns, bf16, 32
@@ -347,7 +528,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd(const uint16_t* __restrict_
     const u32x4* Bb = Bs + buf * kChunks;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int sw = (2 * ks + h) ^ (l32 & 7);
+      const int sw = (2 * ks + h) ^ a_swz(l32);
       bf16x8 af[4], bfr[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) af[i] = as_bf16x8(Ab[(128 * wm + 32 * i + l32) * 8 + sw]);
@@ -440,8 +621,12 @@ hipError_t launch_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K, c
     return launch_fwd_small(x, M, N, K, packed, qscale, step, static_cast<const float*>(lora),
                             static_cast<int>(lora_splits(M, K)), rp, B, r, scale, y, cb, stream);
   const int64_t tiles = cdiv(M, kTile) * cdiv(N, kTile);
-  hipLaunchKernelGGL(k_gemm_fwd, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, x, M, N, K, packed,
-                     qscale, step, static_cast<const uint16_t*>(lora), rp, B, r, scale, y, cb);
+  if (K % 256 == 0)
+    hipLaunchKernelGGL(k_gemm_fwd<true>, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, x, M, N, K,
+                       packed, qscale, step, static_cast<const uint16_t*>(lora), rp, B, r, scale, y, cb);
+  else
+    hipLaunchKernelGGL(k_gemm_fwd<false>, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, x, M, N, K,
+                       packed, qscale, step, static_cast<const uint16_t*>(lora), rp, B, r, scale, y, cb);
   return hipGetLastError();
 }
 

@@ -349,3 +349,54 @@ def test_full_size_sampled(qops, name, M):
     ref = gemm.backward_dx_at(ms, ks, inp["dy"], lambda k: wd[:, int(k)], inp["A"], inp["B"], alpha, r)
     got = to_f64(dx[ms, ks])
     assert rel_fro(got, ref) <= TIGHT
+
+
+# ---------------------------------------------------------------------------
+# full-size configs, every output: the fused kernels against the standalone
+# dequantization (bit-exact to the oracle, above) followed by an fp32 matmul,
+# and bitwise repeatability. Sampling alone can miss errors confined to a few
+# tiles (a stale operand in one workgroup), so every element is bounded:
+#   |got - ref| <= 2^-8 |ref| + 2^-12 S + 2^-8 (alpha/r) T
+# with S = sum_k |a_k||b_k| of the base product (fp32 accumulation-order
+# slack) and T = sum_j |t_j||B_nj| of the adapter term (t is rounded to bf16
+# on both sides; its fp32 sums may round to neighbouring bf16 values).
+# ---------------------------------------------------------------------------
+TILED = ["7b_mlp_up", "7b_mlp_down", "65b_up", "65b_attn"]
+
+
+def _elementwise_ok(got, ref, S, T, scale):
+    bound = ref.abs() * 2.0 ** -8 + S * 2.0 ** -12 + T * (scale * 2.0 ** -8) + 1e-6
+    bad = ((got - ref).abs() > bound).sum().item()
+    return bad
+
+
+@pytest.mark.parametrize("name", TILED)
+def test_full_size_every_output(qops, name):
+    inp = synth.config_inputs(name, None)
+    M, N, K, r, alpha = inp["M"], inp["N"], inp["K"], inp["r"], inp["alpha"]
+    scale = alpha / r
+    qw = gpu_quant(qops, inp["w"])
+    wd = qops.dequant(qw).float()
+    x, A, B = dev(inp["x"]), dev(inp["A"]), dev(inp["B"])
+    y1 = qops.lora_fwd(x, qw, A, B, alpha)
+    y2 = qops.lora_fwd(x, qw, A, B, alpha)
+    assert torch.equal(y1, y2)
+    xf, Af, Bf = x.float(), A.float(), B.float()
+    t = (xf @ Af.t()).bfloat16().float()
+    ref = xf @ wd.t() + scale * (t @ Bf.t())
+    S = xf.abs() @ wd.abs().t()
+    T = t.abs() @ Bf.abs().t()
+    assert _elementwise_ok(y1.float(), ref, S, T, scale) == 0
+    del y1, y2, ref, S, T, t
+    dy = dev(inp["dy"])
+    d1 = qops.bwd_dx(dy, qw, A, B, alpha)
+    d2 = qops.bwd_dx(dy, qw, A, B, alpha)
+    assert torch.equal(d1, d2)
+    dyf = dy.float()
+    u = (dyf @ Bf).bfloat16().float()
+    ref = dyf @ wd + scale * (u @ Af)
+    S = dyf.abs() @ wd.abs()
+    T = u.abs() @ Af.abs()
+    assert _elementwise_ok(d1.float(), ref, S, T, scale) == 0
+    del qw, wd
+    torch.cuda.empty_cache()
