@@ -35,6 +35,7 @@ namespace qnf4 {
 // those (rare) elements take the exact rule.
 // ---------------------------------------------------------------------------
 constexpr int kCells = 129;
+constexpr int64_t kQuantGrid = 512;            // k_quantize workgroups (2 per CU)
 
 struct CellEntry {
   float thr;      // the threshold inside this cell, or +inf
@@ -86,12 +87,15 @@ __device__ void build_lut(CellEntry* lut, const Codebook& cb) {
 
 // max over the 16 lanes of a row (DPP row rotations, then quad permutes) of
 // non-negative floats, compared as their bit patterns (same order)
+// (every lane of these patterns has a source, so bound_ctrl never applies; it
+// and the zero `old` let the compiler fold each move into the max as a DPP
+// operand)
 __device__ __forceinline__ float row16_max_nonneg(float a) {
   uint32_t x = __builtin_bit_cast(uint32_t, a);
-  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(x), static_cast<int>(x), 0x128, 0xF, 0xF, false)));
-  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(x), static_cast<int>(x), 0x124, 0xF, 0xF, false)));
-  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(x), static_cast<int>(x), 0xB1, 0xF, 0xF, false)));
-  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(x), static_cast<int>(x), 0x4E, 0xF, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x128, 0xF, 0xF, true)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x124, 0xF, 0xF, true)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0xB1, 0xF, 0xF, true)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x4E, 0xF, 0xF, true)));
   return __builtin_bit_cast(float, x);
 }
 
@@ -115,99 +119,128 @@ struct Load4<uint16_t> {
 };
 
 // ---------------------------------------------------------------------------
-// k_quantize: one 256-thread workgroup per group of 256 blocks (16384
-// weights). 16 rounds of 16 blocks, 16 lanes per block and 4 consecutive
-// weights per lane; all 16 rounds of loads are issued before any is used.
-// With DQ the group's constants are double-quantized in the same pass.
+// k_quantize: a group of 256 blocks (16384 weights) at a time per 256-thread
+// workgroup, groups taken grid-stride. A group is two halves of 8 rounds; a
+// round is 16 blocks, 16 lanes per block and 4 consecutive weights per lane.
+// The loads of the next half are in flight while the current half is coded,
+// so the coding arithmetic overlaps the weight stream instead of following
+// it. With DQ the group's constants are double-quantized in the same pass.
 // ---------------------------------------------------------------------------
 template <typename Tin, bool DQ>
 __global__ __launch_bounds__(256) void k_quantize(const Tin* __restrict__ w, int64_t nblocks,
                                                   uint16_t* __restrict__ packed16,
                                                   float* __restrict__ absmax, int8_t* __restrict__ qscale,
-                                                  float* __restrict__ step, Codebook cb) {
+                                                  float* __restrict__ step, Codebook cb, int64_t gstride) {
+  // gstride == gridDim.x, passed as an argument: reading gridDim.x inside the
+  // loop is a vector load from the dispatch packet, and waiting for it would
+  // drain the prefetched weight loads
   __shared__ CellEntry lut[kCells];
   __shared__ float amax_s[256];
   __shared__ float wmax[4];
   const int t = threadIdx.x, lane16 = t & 15, sub = t >> 4;
-  const int64_t g = blockIdx.x;
-  const int64_t b0 = g * 256;
-  const int nb_here = static_cast<int>(nblocks - b0 < 256 ? nblocks - b0 : 256);
-  f32x4 v[16];
+  const int64_t ngroups = (nblocks + 255) / 256;
+  int64_t g = blockIdx.x;
+  if (g >= ngroups) return;
+  auto nb_in = [&](int64_t gg) { return static_cast<int>(nblocks - gg * 256 < 256 ? nblocks - gg * 256 : 256); };
+  // rounds 8 hh .. 8 hh + 7 of group gg
+  auto load_half = [&](int64_t gg, int hh, f32x4 (&v)[8]) {
+    const int nbh = nb_in(gg);
 #pragma unroll
-  for (int rd = 0; rd < 16; ++rd) {
-    const int bl = rd * 16 + sub;
-    const int64_t b = b0 + (bl < nb_here ? bl : 0);
-    v[rd] = Load4<Tin>::at(w + b * 64 + lane16 * 4);
-  }
+    for (int i = 0; i < 8; ++i) {
+      const int bl = (8 * hh + i) * 16 + sub;
+      const int64_t b = gg * 256 + (bl < nbh ? bl : 0);
+      v[i] = Load4<Tin>::at(w + b * 64 + lane16 * 4);
+    }
+  };
+  // fast path for the 32 elements of this thread in a half; a round with any
+  // element near a threshold (or a zero / tiny block) is flagged for the exact
+  // rule
+  auto code_half = [&](int64_t gg, int hh, const f32x4 (&v)[8], uint32_t& redo) {
+    const int nbh = nb_in(gg);
+    const bool full = nbh == 256;                // every group but possibly the last
+    uint16_t* pk = packed16 + (gg * 256 + sub) * 16 + lane16;   // round rd: + rd * 256
+    float* am = absmax + gg * 256 + sub;                         // round rd: + rd * 16
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rd = 8 * hh + i;
+      const int bl = rd * 16 + sub;
+      const float a = row16_max_nonneg(fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)),
+                                             fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+      const bool fast = a >= 1e-30f;             // uniform over the block's 16 lanes
+      const float ra = fast ? __builtin_amdgcn_rcpf(a) : 0.0f;
+      uint32_t word = 0;
+      float dmin = fast ? __builtin_inff() : 0.0f;   // distance of the nearest element to its threshold
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float we = e == 0 ? v[i].x : e == 1 ? v[i].y : e == 2 ? v[i].z : v[i].w;
+        const float vp = we * ra;
+        const CellEntry ce = lut[cell_of(vp)];
+        word |= (static_cast<uint32_t>(ce.base) + (vp > ce.thr ? 1u : 0u)) << (4 * e);
+        dmin = fminf(dmin, fabsf(vp - ce.thr));   // inf - inf cannot occur: vp is finite
+      }
+      redo |= (dmin > 1e-6f) ? 0u : (1u << rd);
+      asm volatile("" ::"v"(redo));              // keep the check in this round (register pressure)
+      if (full || bl < nbh) {
+        pk[rd * 256] = static_cast<uint16_t>(word);
+        if (lane16 == 0) {
+          am[rd * 16] = a;
+          amax_s[bl] = a;
+        }
+      }
+    }
+  };
+  f32x4 va[8], vb[8];
+  load_half(g, 0, va);
   build_lut(lut, cb);
   __syncthreads();
-  // fast path for all 64 elements of this thread; a round with any element
-  // near a threshold (or a zero / tiny block) is flagged and redone exactly
-  uint32_t redo = 0;
-#pragma unroll
-  for (int rd = 0; rd < 16; ++rd) {
-    const int bl = rd * 16 + sub;
-    const float a = row16_max_nonneg(fmaxf(fmaxf(fabsf(v[rd].x), fabsf(v[rd].y)),
-                                           fmaxf(fabsf(v[rd].z), fabsf(v[rd].w))));
-    const bool fast = a >= 1e-30f;               // uniform over the block's 16 lanes
-    const float ra = fast ? __builtin_amdgcn_rcpf(a) : 0.0f;
-    uint32_t word = 0;
-    bool near = !fast;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float we = e == 0 ? v[rd].x : e == 1 ? v[rd].y : e == 2 ? v[rd].z : v[rd].w;
-      const float vp = we * ra;
-      const CellEntry ce = lut[cell_of(vp)];
-      word |= (static_cast<uint32_t>(ce.base) + (vp > ce.thr ? 1u : 0u)) << (4 * e);
-      near = near || !(fabsf(vp - ce.thr) > 1e-6f);
-    }
-    redo |= near ? (1u << rd) : 0u;
-    asm volatile("" ::"v"(redo));                // keep the check in this round (register pressure)
-    if (bl < nb_here) {
-      const int64_t b = b0 + bl;
-      packed16[b * 16 + lane16] = static_cast<uint16_t>(word);
-      if (lane16 == 0) {
-        absmax[b] = a;
-        amax_s[bl] = a;
+  for (; g < ngroups; g += gstride) {
+    const int nb_here = nb_in(g);
+    load_half(g, 1, vb);
+    uint32_t redo = 0;
+    code_half(g, 0, va, redo);
+    // next group's first half (the last group re-loads itself: no branch, so
+    // no wait for this group's second half before these loads issue)
+    load_half(g + gstride < ngroups ? g + gstride : g, 0, va);
+    code_half(g, 1, vb, redo);
+    __syncthreads();                             // amax_s complete
+    if (redo) {                                  // rare: exact rule for the flagged rounds
+#pragma unroll 1
+      for (int rd = 0; rd < 16; ++rd) {
+        const int bl = rd * 16 + sub;
+        if (!(redo & (1u << rd)) || bl >= nb_here) continue;
+        const int64_t b = g * 256 + bl;
+        const f32x4 x = Load4<Tin>::at(w + b * 64 + lane16 * 4);
+        const float a = amax_s[bl];
+        uint32_t word = 0;
+#pragma unroll 1
+        for (int e = 0; e < 4; ++e) {
+          const float we = e == 0 ? x.x : e == 1 ? x.y : e == 2 ? x.z : x.w;
+          word |= exact_code(we, a, cb) << (4 * e);
+        }
+        packed16[b * 16 + lane16] = static_cast<uint16_t>(word);
       }
     }
-  }
-  __syncthreads();                               // amax_s complete
-  if (redo) {                                    // rare: exact rule for the flagged rounds
-#pragma unroll 1
-    for (int rd = 0; rd < 16; ++rd) {
-      const int bl = rd * 16 + sub;
-      if (!(redo & (1u << rd)) || bl >= nb_here) continue;
-      const int64_t b = b0 + bl;
-      const f32x4 x = Load4<Tin>::at(w + b * 64 + lane16 * 4);
-      const float a = amax_s[bl];
-      uint32_t word = 0;
-#pragma unroll 1
-      for (int e = 0; e < 4; ++e) {
-        const float we = e == 0 ? x.x : e == 1 ? x.y : e == 2 ? x.z : x.w;
-        word |= exact_code(we, a, cb) << (4 * e);
+    if (DQ) {
+      // double quantization of this group's constants (same arithmetic as k_dq_scales)
+      const float a = t < nb_here ? amax_s[t] : 0.0f;
+      float m = a;
+      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+      if ((t & 63) == 0) wmax[t >> 6] = m;
+      __syncthreads();
+      m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+      const float d = m / 127.0f;
+      if (t < nb_here) {
+        int q = 0;
+        if (d != 0.0f) {
+          const float r = fminf(fmaxf(__builtin_rintf(a / d), -127.0f), 127.0f);
+          q = static_cast<int>(r);
+        }
+        qscale[g * 256 + t] = static_cast<int8_t>(q);
       }
-      packed16[b * 16 + lane16] = static_cast<uint16_t>(word);
+      if (t == 0) step[g] = d;
     }
+    __syncthreads();                             // amax_s / wmax free for the next group
   }
-  if (!DQ) return;
-  // double quantization of this group's constants (same arithmetic as k_dq_scales)
-  const float a = t < nb_here ? amax_s[t] : 0.0f;
-  float m = a;
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  if ((t & 63) == 0) wmax[t >> 6] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  const float d = m / 127.0f;
-  if (t < nb_here) {
-    int q = 0;
-    if (d != 0.0f) {
-      const float r = fminf(fmaxf(__builtin_rintf(a / d), -127.0f), 127.0f);
-      q = static_cast<int>(r);
-    }
-    qscale[b0 + t] = static_cast<int8_t>(q);
-  }
-  if (t == 0) step[g] = d;
 }
 
 // ---------------------------------------------------------------------------
@@ -272,21 +305,29 @@ static int grid_for(int64_t work_items, int per_block) {
 hipError_t launch_quantize(const void* w, int wdt, int64_t numel, uint8_t* packed, float* absmax,
                            int8_t* qscale, float* step, const Codebook& cb, hipStream_t stream) {
   const int64_t nb = numel / 64;
-  const dim3 grid(static_cast<unsigned>((nb + 255) / 256));
+  // two groups or more per workgroup once there are enough groups to fill
+  // the chip: each workgroup then overlaps one group's coding with the next
+  // group's loads
+  const int64_t ngroups = (nb + 255) / 256;
+  const dim3 grid(static_cast<unsigned>(ngroups < kQuantGrid ? ngroups : kQuantGrid));
   uint16_t* p16 = reinterpret_cast<uint16_t*>(packed);
   const bool dq = qscale != nullptr;
   if (wdt == 0) {
     const float* wf = static_cast<const float*>(w);
     if (dq)
-      hipLaunchKernelGGL((k_quantize<float, true>), grid, dim3(256), 0, stream, wf, nb, p16, absmax, qscale, step, cb);
+      hipLaunchKernelGGL((k_quantize<float, true>), grid, dim3(256), 0, stream, wf, nb, p16, absmax, qscale, step, cb,
+                         static_cast<int64_t>(grid.x));
     else
-      hipLaunchKernelGGL((k_quantize<float, false>), grid, dim3(256), 0, stream, wf, nb, p16, absmax, qscale, step, cb);
+      hipLaunchKernelGGL((k_quantize<float, false>), grid, dim3(256), 0, stream, wf, nb, p16, absmax, qscale, step, cb,
+                         static_cast<int64_t>(grid.x));
   } else {
     const uint16_t* wb = static_cast<const uint16_t*>(w);
     if (dq)
-      hipLaunchKernelGGL((k_quantize<uint16_t, true>), grid, dim3(256), 0, stream, wb, nb, p16, absmax, qscale, step, cb);
+      hipLaunchKernelGGL((k_quantize<uint16_t, true>), grid, dim3(256), 0, stream, wb, nb, p16, absmax, qscale, step, cb,
+                         static_cast<int64_t>(grid.x));
     else
-      hipLaunchKernelGGL((k_quantize<uint16_t, false>), grid, dim3(256), 0, stream, wb, nb, p16, absmax, qscale, step, cb);
+      hipLaunchKernelGGL((k_quantize<uint16_t, false>), grid, dim3(256), 0, stream, wb, nb, p16, absmax, qscale, step, cb,
+                         static_cast<int64_t>(grid.x));
   }
   return hipGetLastError();
 }
