@@ -198,9 +198,11 @@ __global__ __launch_bounds__(256) void k_quantize(const Tin* __restrict__ w, int
     load_half(g, 1, vb);
     uint32_t redo = 0;
     code_half(g, 0, va, redo);
-    // next group's first half (the last group re-loads itself: no branch, so
-    // no wait for this group's second half before these loads issue)
-    load_half(g + gstride < ngroups ? g + gstride : g, 0, va);
+    // next group's first half; the last group instead re-loads its own second
+    // half, which is still in L2 (no branch, so no wait for this group's
+    // second half before these loads issue)
+    const bool more = g + gstride < ngroups;
+    load_half(more ? g + gstride : g, more ? 0 : 1, va);
     code_half(g, 1, vb, redo);
     __syncthreads();                             // amax_s complete
     if (redo) {                                  // rare: exact rule for the flagged rounds
