@@ -444,17 +444,33 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd(const uint16_t* __restrict_
   }
 }
 
-// B tile of the backward: 64 weight rows x 256 output columns, bf16, 32
-// chunks per row. Within each 8-chunk (64-column) group the chunk index is
-// xor-ed with g(row, group): bits 2..1 separate 4 consecutive rows (the rows
-// one transposed read touches) and bit 0 separates neighbouring rows, which
-// keeps both the producer's 16-byte writes and the 8-byte transposed reads
-// spread over the banks.
-__device__ __forceinline__ int bw_slot(int row, int ch) {
-  const int grp = ch >> 3;
-  const int g = ((((row & 3) ^ grp) & 3) << 1) | (row & 1);
-  return row * 32 + (ch ^ g);
-}
+// ---------------------------------------------------------------------------
+// k_gemm_bwd: dX [M, K] = dY . W' (+ LoRA), M > 16.
+//
+// Workgroup tile 256 (M) x 256 (K), four waves as 2 x 2, each 128 x 128:
+// 4 x 4 blocks of 32x32x16 bf16 MFMA. The contraction runs over W's rows (N)
+// in steps of 64, so the weights are needed transposed: each step the
+// workgroup decodes the 64 x 256 slice of W' (one 64-block per thread) into
+// LDS, row-major, and the waves read their B operands with ds_read_b64_tr_b16.
+// Per step k:
+//   dY    tile k+1 (256 x 64) requested by DMA into the other slot of a
+//         two-slot ring (buffer_load ... lds; rows past M read as zero);
+//   codes of step k+2 loaded into registers (128 contiguous bytes per weight
+//         row, four threads a row);
+//   the MFMAs of step k run while the codes of step k+1 are decoded and
+//         written into the other W' buffer.
+// LDS: 2 x 32 KB (dY) + 2 x 36 KB (W', rows padded to 576 bytes so that a
+// transposed read of 4 rows x 64 bytes covers all 64 banks once).
+// ---------------------------------------------------------------------------
+constexpr int kBwRow = 36;                     // 16-byte chunks per LDS row of the W' tile (32 + pad)
+constexpr int kBwChunks = 64 * kBwRow;
+
+struct BCodes {
+  u32x4 p0, p1;    // the 32 code bytes of this thread's block
+  float d;
+  int8_t q;
+  float live;      // 1 for a real weight row, 0 past N
+};
 
 __global__ __launch_bounds__(256, 1) void k_gemm_bwd(const uint16_t* __restrict__ dy, int64_t M, int64_t N,
                                                      int64_t K, const uint8_t* __restrict__ packed,
@@ -463,55 +479,64 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd(const uint16_t* __restrict_
                                                      const uint16_t* __restrict__ ul, int rp,
                                                      const uint16_t* __restrict__ Al, int r, float scale,
                                                      uint16_t* __restrict__ dx, Codebook cb) {
-  __shared__ u32x4 smem[4 * kChunks];
-  u32x4* As = smem;
-  u32x4* Bs = smem + 2 * kChunks;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  __shared__ u32x4 As0[kChunks];
+  __shared__ u32x4 As1[kChunks];
+  __shared__ u32x4 Ws0[kBwChunks];
+  __shared__ u32x4 Ws1[kBwChunks];
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = w >> 1, wn = w & 1;
   const int h = lane >> 5, l32 = lane & 31;
   const int ntm = static_cast<int>(cdiv(M, kTile)), ntk = static_cast<int>(cdiv(K, kTile));
   int tm, tk;
   tile_of(blockIdx.x, ntm, ntk, tm, tk);
+  tm = __builtin_amdgcn_readfirstlane(tm);
+  tk = __builtin_amdgcn_readfirstlane(tk);
   const int64_t m0 = static_cast<int64_t>(tm) * kTile, k0 = static_cast<int64_t>(tk) * kTile;
   const int64_t nbr = K / 64;
   const int64_t nsteps = cdiv(N, 64);
 
-  // A (dY) staging: row arow0 + 32i, contraction chunk ach
+  // dY tile staging through registers (not LDS DMA: the transposed LDS reads
+  // of W' carry no alias information, so any LDS DMA in flight would make the
+  // compiler wait for it before each of them). Thread t moves 16-byte chunk
+  // t & 7 of rows (t >> 3) + 32 i: eight lanes cover a row's 128 bytes.
+  // Buffer loads through a descriptor over this tile's dY rows: rows past M
+  // read as zero without a branch. (Columns past N in the last step read the
+  // next row; the matching weight rows are dead, so they contribute zero.)
   const int ach = t & 7, arow0 = t >> 3;
-  const uint16_t* aptr[8];
+  const int64_t rows_valid = imin(static_cast<int64_t>(kTile), M - m0);
+  const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(dy + m0 * N), 0, static_cast<int>(rows_valid * N * 2), kBufferDword3);
+  uint32_t aoff[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) aptr[i] = dy + imin(m0 + arow0 + 32 * i, M - 1) * N + ach * 8;
-  // B staging: weight row nn of the step, 64-column group kb of the tile
-  const int bnn = t >> 2, bkb = t & 3;
-  const int64_t bkbi = imin(k0 / 64 + bkb, nbr - 1);
-
+  for (int i = 0; i < 8; ++i) aoff[i] = static_cast<uint32_t>((arow0 + 32 * i) * N * 2 + 16 * ach);
   u32x4 areg[8];
-  u32x4 b0, b1;
-  int8_t qv;
-  float dv;
-  auto gload = [&](int64_t st) {
-    const int64_t nbase = st * 64;
-    const bool aval = nbase + ach * 8 < N;
+  auto load_a = [&](int64_t st) {
+    const uint32_t so = static_cast<uint32_t>(imin(st, nsteps - 1) * 128);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) areg[i] = aval ? ld16(aptr[i] + nbase) : u32x4{0u, 0u, 0u, 0u};
-    const int64_t row = imin(nbase + bnn, N - 1);
-    const uint8_t* p = packed + row * (K / 2) + bkbi * 32;
-    b0 = ld16(p);
-    b1 = ld16(p + 16);
-    const int64_t blk = row * nbr + bkbi;
-    qv = qscale[blk];
-    dv = step[blk >> 8];
+    for (int i = 0; i < 8; ++i)
+      areg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(yr, aoff[i], so, 0));
   };
-  auto lstore = [&](int buf) {
-    u32x4* Ab = As + buf * kChunks;
-    u32x4* Bb = Bs + buf * kChunks;
+  auto store_a = [&](u32x4* Ab) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) Ab[a_slot(arow0 + 32 * i, ach)] = areg[i];
-    const MagTable tb = make_table(cb, block_scale(qv, dv));
-    const uint32_t pw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-    for (int ch = 0; ch < 8; ++ch) Bb[bw_slot(bnn, 8 * bkb + ch)] = decode8(pw[ch], tb);
   };
+  // this thread decodes weight row (t >> 2) of the step, 64-column block t & 3
+  const int brow = t >> 2, bkb = t & 3;
+  const int64_t bkbi = imin(k0 / 64 + bkb, nbr - 1);
+  auto load_codes = [&](int64_t st, BCodes& P) {
+    const int64_t n = st * 64 + brow;
+    const int64_t nc = imin(n, N - 1);
+    const uint8_t* pp = packed + nc * (K / 2) + bkbi * 32;
+    P.p0 = ld16(pp);
+    P.p1 = ld16(pp + 16);
+    const int64_t blk = nc * nbr + bkbi;
+    P.q = qscale[blk];
+    P.d = step[blk >> 8];
+    P.live = n < N ? 1.0f : 0.0f;
+  };
+  // W' tile slot of (row, 16-byte chunk c of the 256 columns)
+  auto w_slot = [](int row, int c) { return row * kBwRow + c; };
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -521,46 +546,112 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd(const uint16_t* __restrict_
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+  // B-operand reads (ds_read_b64_tr_b16): lane group G = lane / 16 reads rows
+  // 16 s + 8 (G >> 1) + 4 q + (j16 >> 2), 4 columns at 4 (j16 & 3) of the
+  // 16-column half (G & 1) of the wave's 32-column block j
   const int G = lane >> 4, j16 = lane & 15;
   const int hh = G >> 1, cbh = G & 1;
-  auto compute = [&](int buf) {
-    const u32x4* Ab = As + buf * kChunks;
-    const u32x4* Bb = Bs + buf * kChunks;
+  auto read_b = [&](const u32x4* Wb, int s, bf16x8 (&bf)[4]) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int sw = (2 * ks + h) ^ a_swz(l32);
-      bf16x8 af[4], bfr[4];
+    for (int j = 0; j < 4; ++j) {
+      const int col = 128 * wn + 32 * j + 16 * cbh + 4 * (j16 & 3);
+      s16x4 v[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = as_bf16x8(Ab[(128 * wm + 32 * i + l32) * 8 + sw]);
+      for (int q = 0; q < 2; ++q) {
+        const int row = 16 * s + 8 * hh + 4 * q + (j16 >> 2);
+        v[q] = ds_read_tr(Wb, w_slot(row, col >> 3) * 8 + (col & 4));
+      }
+      bf[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  auto read_a = [&](const u32x4* Ab, int s, bf16x8 (&af)[4]) {
+    const int sw = (2 * s + h) ^ a_swz(l32);       // a_swz(128 wm + 32 i + l32) == a_swz(l32)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = 128 * wn + 32 * j + 16 * cbh + 4 * (j16 & 3);
-        s16x4 v[2];
+    for (int i = 0; i < 4; ++i) af[i] = as_bf16x8(Ab[(128 * wm + 32 * i + l32) * 8 + sw]);
+  };
+
+  // one step: MFMAs on (Ab, Wb); decode `nx` into Wn; load dY tile st+1 and
+  // write it into An in the last sub-step; load the codes of step st+2 into `ld`
+  auto step_b = [&](const u32x4* Ab, u32x4* An, const u32x4* Wb, u32x4* Wn, const BCodes& nx, BCodes& ld,
+                    int64_t st) {
+    load_a(st + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_codes(st + 2, ld);
+    __builtin_amdgcn_sched_barrier(0);
+    const MagTable tb = make_table(cb, block_scale(nx.q, nx.d) * nx.live);
+    const uint32_t pw[8] = {nx.p0.x, nx.p0.y, nx.p0.z, nx.p0.w, nx.p1.x, nx.p1.y, nx.p1.z, nx.p1.w};
+    bf16x8 af[2][4], bf[2][4];
+    read_a(Ab, 0, af[0]);
+    read_b(Wb, 0, bf[0]);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int row = 16 * ks + 8 * hh + 4 * q + (j16 >> 2);
-          v[q] = ds_read_tr(Bb, bw_slot(row, col >> 3) * 8 + (col & 4));
-        }
-        bfr[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    for (int s = 0; s < 4; ++s) {
+      if (s < 3) {
+        read_a(Ab, s + 1, af[(s + 1) & 1]);
+        read_b(Wb, s + 1, bf[(s + 1) & 1]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[s & 1][i], bf[s & 1][j], acc[i][j]);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) Wn[w_slot(brow, 8 * bkb + 2 * s + c)] = decode8(pw[2 * s + c], tb);
+      if (s == 3) store_a(An);
     }
+    // issue order: all fragment reads of a sub-step at the start of the one
+    // before it (the compiler waits for ds_read_b64_tr_b16 with lgkmcnt(0) at
+    // the first use, so they must be long in flight by then), then per MFMA
+    // about four VALU ops of the decode; each sub-step's two W' writes at its
+    // end and the eight dY writes in the last sub-step. (Mask 0x080, all LDS
+    // ops: the transposed reads do not count as plain LDS reads.)
+    auto sub_mfmas = [] {
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+    };
+    __builtin_amdgcn_sched_group_barrier(0x080, 24, 0);
+    sub_mfmas();
+    __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x080, 12, 0);
+    sub_mfmas();
+    __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x080, 12, 0);
+    sub_mfmas();
+    __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+    sub_mfmas();
+    __builtin_amdgcn_sched_group_barrier(0x200, 10, 0);
   };
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int64_t st = 0; st < nsteps; ++st) {
-    const int cur = static_cast<int>(st & 1);
-    const bool more = st + 1 < nsteps;
-    if (more) gload(st + 1);
-    compute(cur);
-    if (more) lstore(cur ^ 1);
-    __syncthreads();
+  // prologue: dY tile 0, codes of steps 0 and 1; decode step 0
+  BCodes P0, P1;
+  load_a(0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_codes(0, P0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_codes(1, P1);
+  __builtin_amdgcn_sched_barrier(0);
+  store_a(As0);
+  asm volatile("" ::"v"(P1.p0), "v"(P1.p1), "v"(static_cast<int>(P1.q)), "v"(P1.d));
+  {
+    const MagTable tb = make_table(cb, block_scale(P0.q, P0.d) * P0.live);
+    const uint32_t pw[8] = {P0.p0.x, P0.p0.y, P0.p0.z, P0.p0.w, P0.p1.x, P0.p1.y, P0.p1.z, P0.p1.w};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) Ws0[w_slot(brow, 8 * bkb + c)] = decode8(pw[c], tb);
   }
+  __syncthreads();
+  // The end of step st waits for this wave's LDS writes (W' and dY of step
+  // st+1), then the barrier publishes them; the code loads of step st+2 stay
+  // in flight.
+  for (int64_t st = 0; st < nsteps; st += 2) {
+    step_b(As0, As1, Ws0, Ws1, P1, P0, st);
+    __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0)
+    lds_barrier();
+    step_b(As1, As0, Ws1, Ws0, P0, P1, st + 1);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    lds_barrier();
+  }
+  wait_vm<0>();
 
   if (r > 0) {
 #pragma unroll
@@ -588,17 +679,28 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd(const uint16_t* __restrict_
       }
     }
   }
+  if (m0 + kTile <= M && k0 + kTile <= K) {
+    uint16_t* dt = dx + (m0 + 128 * wm + 4 * h) * K + k0 + 128 * wn + l32;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t kk = k0 + 128 * wn + 32 * j + l32;
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t mm = m0 + 128 * wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (mm < M && kk < K) dx[mm * K + kk] = bf16_bits(acc[i][j][v]);
+        for (int v = 0; v < 16; ++v)
+          dt[(32 * i + 8 * (v >> 2) + (v & 3)) * K + 32 * j] = bf16_bits(acc[i][j][v]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t kk = k0 + 128 * wn + 32 * j + l32;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t mm = m0 + 128 * wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (mm < M && kk < K) dx[mm * K + kk] = bf16_bits(acc[i][j][v]);
+        }
       }
-    }
+  }
 }
 
 // ---------------------------------------------------------------------------
