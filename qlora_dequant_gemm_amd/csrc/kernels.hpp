@@ -43,6 +43,7 @@ inline int64_t bwd_small_splits(int64_t N, int64_t K) {
 struct WsLayout {
   size_t lora_off = 0, lora_bytes = 0;    // t or u (bf16 [M][rp], or fp32 partials)
   size_t part_off = 0, part_bytes = 0;    // small-M backward partials
+  size_t bt_off = 0, bt_bytes = 0;        // large-M backward: B transposed, bf16 [r][N]
   size_t total = 0;
 };
 
@@ -60,7 +61,9 @@ inline WsLayout ws_layout(int op, int64_t M, int64_t N, int64_t K, int r) {
   w.part_off = w.lora_bytes;
   if (op == 1 && M <= kSmallM)
     w.part_bytes = align256(static_cast<size_t>(bwd_small_splits(N, K) * M * K * 4));
-  w.total = w.lora_bytes + w.part_bytes;
+  w.bt_off = w.part_off + w.part_bytes;
+  if (op == 1 && M > kSmallM && r > 0) w.bt_bytes = align256(static_cast<size_t>(r) * N * 2);
+  w.total = w.lora_bytes + w.part_bytes + w.bt_bytes;
   return w;
 }
 
@@ -75,8 +78,9 @@ hipError_t launch_dequant(const uint8_t* packed, const int8_t* qscale, const flo
 
 // rank-r down projection of `in` [M][Kc] by the adapter (wrow: A [r][Kc];
 // else B [Kc][r]); M <= kSmallM writes lora_splits fp32 partials, else bf16.
+// wt: workspace for the transposed adapter (large M, wrow == false; r * Kc bf16)
 hipError_t launch_lora_down(bool wrow, const uint16_t* in, int64_t M, int64_t Kc, const uint16_t* W, int r,
-                            void* out, hipStream_t stream);
+                            void* out, hipStream_t stream, uint16_t* wt);
 hipError_t launch_fwd_small(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
                             const int8_t* qscale, const float* step, const float* tpart, int St, int rp,
                             const uint16_t* B, int r, float scale, uint16_t* y, const Codebook& cb,

@@ -34,7 +34,11 @@ __device__ __forceinline__ u32x4 adapter8(const uint16_t* __restrict__ W, int64_
 // 16 rows and take the 32-deep contraction steps round robin (operands straight
 // from global memory; the adapter stays in L2), then reduce through LDS.
 // ---------------------------------------------------------------------------
-template <bool WROW>
+// NT: 16-wide rank tiles holding real ranks (ceil(r / 16)); the padding
+// columns up to rp are written as zero. Each wave takes 32-deep contraction
+// steps round robin in groups of 8, all of a group's loads issued before its
+// MFMAs, so that enough loads are in flight to stream `in` from HBM.
+template <int NT>
 __global__ __launch_bounds__(256) void k_lora_down(const uint16_t* __restrict__ in, int64_t M, int64_t Kc,
                                                    const uint16_t* __restrict__ W, int r, int rp,
                                                    uint16_t* __restrict__ out) {
@@ -48,13 +52,21 @@ __global__ __launch_bounds__(256) void k_lora_down(const uint16_t* __restrict__ 
   f32x4 acc[8];
 #pragma unroll
   for (int jt = 0; jt < 8; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int64_t st = w; st < nsteps; st += 4) {
-    const int64_t k = st * 32 + 8 * g;
-    const bf16x8 a = as_bf16x8(k < Kc ? ld16(in_row + k) : u32x4{0u, 0u, 0u, 0u});
+  constexpr int kGroup = 8;
+  for (int64_t st0 = w * kGroup; st0 < nsteps; st0 += 4 * kGroup) {
+    u32x4 xa[kGroup], wa[kGroup][NT];
 #pragma unroll
-    for (int jt = 0; jt < 8; ++jt)
-      if (jt < ntile) acc[jt] = mfma16(a, as_bf16x8(adapter8<WROW>(W, Kc, r, 16 * jt + c, k)), acc[jt]);
+    for (int u = 0; u < kGroup; ++u) {
+      const int64_t k = (st0 + u) * 32 + 8 * g;
+      const bool kin = st0 + u < nsteps && k < Kc;
+      xa[u] = kin ? ld16(in_row + k) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt) wa[u][jt] = kin ? adapter8<true>(W, Kc, r, 16 * jt + c, k) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u)
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt) acc[jt] = mfma16(as_bf16x8(xa[u]), as_bf16x8(wa[u][jt]), acc[jt]);
   }
 #pragma unroll
   for (int jt = 0; jt < 8; ++jt)
@@ -116,8 +128,17 @@ __global__ __launch_bounds__(512) void k_lora_down_small(const uint16_t* __restr
   }
 }
 
+// B [N][r] -> Bt [r][N] (the large-M backward contracts over N, so it reads
+// the adapter row-major through this copy)
+__global__ __launch_bounds__(256) void k_adapter_t(const uint16_t* __restrict__ B, int64_t N, int r,
+                                                   uint16_t* __restrict__ Bt) {
+  const int64_t n = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (n >= N) return;
+  for (int j = 0; j < r; ++j) Bt[static_cast<int64_t>(j) * N + n] = B[n * r + j];
+}
+
 hipError_t launch_lora_down(bool wrow, const uint16_t* in, int64_t M, int64_t Kc, const uint16_t* W, int r,
-                            void* out, hipStream_t stream) {
+                            void* out, hipStream_t stream, uint16_t* wt) {
   const int rp = static_cast<int>(rank_pad(r));
   if (M <= kSmallM) {
     const int S = static_cast<int>(lora_splits(M, Kc));
@@ -129,12 +150,25 @@ hipError_t launch_lora_down(bool wrow, const uint16_t* in, int64_t M, int64_t Kc
                          static_cast<float*>(out));
   } else {
     const unsigned grid = static_cast<unsigned>(cdiv(M, 16));
-    if (wrow)
-      hipLaunchKernelGGL(k_lora_down<true>, dim3(grid), dim3(256), 0, stream, in, M, Kc, W, r, rp,
-                         static_cast<uint16_t*>(out));
+    const uint16_t* Wr = W;
+    if (!wrow) {
+      hipLaunchKernelGGL(k_adapter_t, dim3(static_cast<unsigned>(cdiv(Kc, 256))), dim3(256), 0, stream, W, Kc, r,
+                         wt);
+      Wr = wt;
+    }
+    const int nt = (r + 15) / 16;
+#define QNF4_LDOWN(NTV)                                                                                   \
+  hipLaunchKernelGGL(k_lora_down<NTV>, dim3(grid), dim3(256), 0, stream, in, M, Kc, Wr, r, rp, \
+                     static_cast<uint16_t*>(out))
+    if (nt <= 1)
+      QNF4_LDOWN(1);
+    else if (nt == 2)
+      QNF4_LDOWN(2);
+    else if (nt <= 4)
+      QNF4_LDOWN(4);
     else
-      hipLaunchKernelGGL(k_lora_down<false>, dim3(grid), dim3(256), 0, stream, in, M, Kc, W, r, rp,
-                         static_cast<uint16_t*>(out));
+      QNF4_LDOWN(8);
+#undef QNF4_LDOWN
   }
   return hipGetLastError();
 }
