@@ -741,15 +741,15 @@ hipError_t launch_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K, co
   const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
   const int rp = r > 0 ? static_cast<int>(rank_pad(r)) : 0;
   void* lora = r > 0 ? static_cast<void*>(wsb + L.lora_off) : nullptr;
+  // small M: the down-projection u = dY . B is computed inside k_bwd_small
+  if (M <= kSmallM)
+    return launch_bwd_small(dy, M, N, K, packed, qscale, step, static_cast<float*>(lora), rp, A, B, r, scale,
+                            reinterpret_cast<float*>(wsb + L.part_off), dx, cb, stream);
   if (r > 0) {
     const hipError_t e = launch_lora_down(false, dy, M, N, B, r, lora, stream,
                                           reinterpret_cast<uint16_t*>(wsb + L.bt_off));
     if (e != hipSuccess) return e;
   }
-  if (M <= kSmallM)
-    return launch_bwd_small(dy, M, N, K, packed, qscale, step, static_cast<const float*>(lora),
-                            static_cast<int>(lora_splits(M, N)), rp, A, r, scale,
-                            reinterpret_cast<float*>(wsb + L.part_off), dx, cb, stream);
   const int64_t tiles = cdiv(M, kTile) * cdiv(K, kTile);
   hipLaunchKernelGGL(k_gemm_bwd, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, dy, M, N, K, packed,
                      qscale, step, static_cast<const uint16_t*>(lora), rp, A, r, scale, dx, cb);

@@ -55,8 +55,10 @@ inline WsLayout ws_layout(int op, int64_t M, int64_t N, int64_t K, int r) {
     const int64_t Kc = op == 0 ? K : N;
     if (M > kSmallM)
       w.lora_bytes = align256(static_cast<size_t>(M * rp * 2));
-    else
+    else if (op == 0)
       w.lora_bytes = align256(static_cast<size_t>(lora_splits(M, Kc) * M * rp * 4));
+    else                                       // u partials, one per row slice of the small-M backward
+      w.lora_bytes = align256(static_cast<size_t>(bwd_small_splits(N, K) * M * rp * 4));
   }
   w.part_off = w.lora_bytes;
   if (op == 1 && M <= kSmallM)
@@ -86,9 +88,9 @@ hipError_t launch_fwd_small(const uint16_t* x, int64_t M, int64_t N, int64_t K, 
                             const uint16_t* B, int r, float scale, uint16_t* y, const Codebook& cb,
                             hipStream_t stream);
 hipError_t launch_bwd_small(const uint16_t* dy, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
-                            const int8_t* qscale, const float* step, const float* upart, int Su, int rp,
-                            const uint16_t* A, int r, float scale, float* part, uint16_t* dx,
-                            const Codebook& cb, hipStream_t stream);
+                            const int8_t* qscale, const float* step, float* upart, int rp, const uint16_t* A,
+                            const uint16_t* B, int r, float scale, float* part, uint16_t* dx, const Codebook& cb,
+                            hipStream_t stream);
 
 hipError_t launch_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
                            const int8_t* qscale, const float* step, const uint16_t* A, const uint16_t* B,

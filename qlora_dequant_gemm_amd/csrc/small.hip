@@ -169,24 +169,54 @@ __device__ __forceinline__ int sm_slot(int row, int ch) {
   return row * 8 + (ch ^ sw);
 }
 
+// Workgroup id -> (column tile kt, row slice s). A 128-byte line of a packed
+// weight row holds the codes of four consecutive column tiles; the four
+// workgroups that share it are given consecutive ids on one XCD (ids go
+// round-robin over the 8 XCDs), so the line is fetched into that XCD's L2
+// once instead of once per tile.
+__device__ __forceinline__ void bwd_tile_of(int lin, int ktiles, int S, int& kt, int& s) {
+  if ((ktiles & 3) == 0 && ((ktiles * S) & 31) == 0) {
+    const int xcd = lin & 7, j = lin >> 3;
+    const int p = 8 * (j >> 2) + xcd;
+    kt = 4 * (p % (ktiles >> 2)) + (j & 3);
+    s = p / (ktiles >> 2);
+  } else {
+    kt = lin % ktiles;
+    s = lin / ktiles;
+  }
+}
+
+// The workgroups of column tile 0 also compute this slice's share of the LoRA
+// down-projection u = dY . B (B [N][r]), from the same dY fragments:
+// upart[s][m][rp] fp32, summed over slices by k_bwd_finish. NTU: rank tiles
+// of 16 (ceil(r / 16), rounded up to a power of two; 0 without an adapter).
+template <int NTU>
 __global__ __launch_bounds__(64 * kBwdWaves) void k_bwd_small(const uint16_t* __restrict__ dy, int64_t M,
                                                               int64_t N, int64_t K,
                                                               const uint8_t* __restrict__ packed,
                                                               const int8_t* __restrict__ qscale,
                                                               const float* __restrict__ step, int S,
-                                                              float* __restrict__ part, Codebook cb) {
+                                                              float* __restrict__ part,
+                                                              const uint16_t* __restrict__ Bl, int r, int rp,
+                                                              float* __restrict__ upart, Codebook cb) {
   __shared__ u32x4 Bs[kBwdRows * 8];         // 128 KB: one step's tile, then the reduction
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int64_t kt = blockIdx.x;             // 64-column tile == block column kt
-  const int s = blockIdx.y;
+  int kti, s;
+  bwd_tile_of(blockIdx.x, static_cast<int>(K / 64), S, kti, s);
+  const int64_t kt = kti;                    // 64-column tile == block column kt
+  const bool do_u = kti == 0 && r > 0;
+  const int ntu = do_u ? (r + 15) / 16 : 0;  // rank tiles of u computed here (<= NTU)
   const int64_t nbr = K / 64;
   const int64_t nsteps = cdiv(N, kBwdRows);
   const int64_t st_beg = s * nsteps / S, st_end = (s + 1) * nsteps / S;
   const int64_t m = imin(static_cast<int64_t>(lane & 15), M - 1);
   const int G = lane >> 4, j16 = lane & 15;
-  f32x4 acc[4];
+  constexpr int kU = NTU > 0 ? NTU : 1;
+  f32x4 acc[4], uacc[kU];
 #pragma unroll
   for (int cbk = 0; cbk < 4; ++cbk) acc[cbk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int jt = 0; jt < kU; ++jt) uacc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int64_t st = st_beg; st < st_end; ++st) {
     // this thread's weight row-block and this wave's dY fragments
     const int64_t row = imin(st * kBwdRows + t, N - 1);
@@ -224,6 +254,28 @@ __global__ __launch_bounds__(64 * kBwdWaves) void k_bwd_small(const uint16_t* __
         acc[cbk] = mfma16(as_bf16x8(av[ks]), bv, acc[cbk]);
       }
     }
+    if (NTU > 0 && do_u) {
+      // B operand of u: lane (rank 16 jt + j16, rows n0 .. n0 + 7 of the
+      // contraction) from B [N][r], zero past N or r
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int64_t n0 = st * kBwdRows + 64 * w + 32 * ks + 8 * G;
+#pragma unroll
+        for (int jt = 0; jt < NTU; ++jt) {
+          if (jt < ntu) {
+            const int j = 16 * jt + j16;
+            uint32_t bv[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int64_t n = n0 + e;
+              const uint32_t val = (n < N && j < r) ? static_cast<uint32_t>(Bl[n * r + j]) : 0u;
+              bv[e >> 1] |= val << (16 * (e & 1));
+            }
+            uacc[jt] = mfma16(as_bf16x8(av[ks]), as_bf16x8(u32x4{bv[0], bv[1], bv[2], bv[3]}), uacc[jt]);
+          }
+        }
+      }
+    }
   }
   __syncthreads();                             // tile reads done: reuse LDS
   f32x4* red = reinterpret_cast<f32x4*>(Bs);   // [wave][cbk][lane]
@@ -239,6 +291,30 @@ __global__ __launch_bounds__(64 * kBwdWaves) void k_bwd_small(const uint16_t* __
     for (int v = 0; v < 4; ++v) {
       const int64_t mm = 4 * (ln >> 4) + v;
       if (mm < M) part[(s * M + mm) * K + kt * 64 + 16 * cbk + (ln & 15)] = sum[v];
+    }
+  }
+  if (NTU > 0 && do_u) {
+    // u partials of this slice: lane (G, j16) of tile jt holds u[4 G + v][16 jt + j16]
+    __syncthreads();
+#pragma unroll
+    for (int jt = 0; jt < NTU; ++jt)
+      if (jt < ntu) red[(w * 8 + jt) * 64 + lane] = uacc[jt];
+    __syncthreads();
+    for (int idx = t; idx < ntu * 64; idx += 64 * kBwdWaves) {
+      const int jt = idx >> 6, ln = idx & 63;
+      f32x4 sum = red[jt * 64 + ln];
+#pragma unroll
+      for (int i = 1; i < kBwdWaves; ++i) sum += red[(i * 8 + jt) * 64 + ln];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t mm = 4 * (ln >> 4) + v;
+        if (mm < M) upart[(s * M + mm) * rp + 16 * jt + (ln & 15)] = sum[v];
+      }
+    }
+    // ranks between ceil(r/16)*16 and rp are zero
+    for (int idx = t; idx < M * rp; idx += 64 * kBwdWaves) {
+      const int rank = idx % rp;
+      if (rank >= 16 * ntu) upart[s * M * rp + idx] = 0.0f;
     }
   }
 }
@@ -257,6 +333,11 @@ __global__ __launch_bounds__(256) void k_bwd_finish(const float* __restrict__ pa
   float v = 0.f;
   for (int s = 0; s < S; ++s) v += part[(s * M + m) * K + kc];
   if (r > 0) {
+    // this column of A, loaded before the barrier (ranks beyond 32 after it)
+    float av[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      av[j] = j < r ? bf16_lo(static_cast<uint32_t>(Al[static_cast<int64_t>(j) * K + kc])) : 0.0f;
     if (t < rp) {
       float u = 0.f;
       for (int s = 0; s < Su; ++s) u += upart[(s * M + m) * rp + t];
@@ -264,8 +345,9 @@ __global__ __launch_bounds__(256) void k_bwd_finish(const float* __restrict__ pa
     }
     __syncthreads();
     float l = 0.f;
-#pragma unroll 8
-    for (int j = 0; j < r; ++j) l += us[j] * bf16_lo(static_cast<uint32_t>(Al[static_cast<int64_t>(j) * K + kc]));
+#pragma unroll
+    for (int j = 0; j < 32; ++j) l += us[j < rp ? j : 0] * av[j];
+    for (int j = 32; j < r; ++j) l += us[j] * bf16_lo(static_cast<uint32_t>(Al[static_cast<int64_t>(j) * K + kc]));
     v += scale * l;
   }
   if (k < K) dx[m * K + k] = bf16_bits(v);
@@ -286,14 +368,28 @@ hipError_t launch_fwd_small(const uint16_t* x, int64_t M, int64_t N, int64_t K, 
 }
 
 hipError_t launch_bwd_small(const uint16_t* dy, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
-                            const int8_t* qscale, const float* step, const float* upart, int Su, int rp,
-                            const uint16_t* A, int r, float scale, float* part, uint16_t* dx,
-                            const Codebook& cb, hipStream_t stream) {
+                            const int8_t* qscale, const float* step, float* upart, int rp, const uint16_t* A,
+                            const uint16_t* B, int r, float scale, float* part, uint16_t* dx, const Codebook& cb,
+                            hipStream_t stream) {
   const int S = static_cast<int>(bwd_small_splits(N, K));
-  hipLaunchKernelGGL(k_bwd_small, dim3(static_cast<unsigned>(K / 64), S), dim3(64 * kBwdWaves), 0, stream, dy, M,
-                     N, K, packed, qscale, step, S, part, cb);
+  const dim3 grid(static_cast<unsigned>((K / 64) * S)), block(64 * kBwdWaves);
+  const int nt = r > 0 ? (r + 15) / 16 : 0;
+#define QNF4_BWDS(NTV)                                                                                        \
+  hipLaunchKernelGGL(k_bwd_small<NTV>, grid, block, 0, stream, dy, M, N, K, packed, qscale, step, S, part, B, r, \
+                     rp, upart, cb)
+  if (nt == 0)
+    QNF4_BWDS(0);
+  else if (nt == 1)
+    QNF4_BWDS(1);
+  else if (nt == 2)
+    QNF4_BWDS(2);
+  else if (nt <= 4)
+    QNF4_BWDS(4);
+  else
+    QNF4_BWDS(8);
+#undef QNF4_BWDS
   hipLaunchKernelGGL(k_bwd_finish, dim3(static_cast<unsigned>(cdiv(K, 256)), static_cast<unsigned>(M)), dim3(256),
-                     0, stream, part, S, M, K, upart, Su, rp, A, r, scale, dx);
+                     0, stream, part, S, M, K, upart, S, rp, A, r, scale, dx);
   return hipGetLastError();
 }
 
