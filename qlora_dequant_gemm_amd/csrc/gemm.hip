@@ -535,8 +535,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd(const uint16_t* __restrict_
     P.d = step[blk >> 8];
     P.live = n < N ? 1.0f : 0.0f;
   };
-  // W' tile slot of (row, 16-byte chunk c of the 256 columns)
-  auto w_slot = [](int row, int c) { return row * kBwRow + c; };
+  // W' tile slot of (row, 16-byte chunk c of the 256 columns). Within each
+  // 8-chunk block the chunk is xor-ed with the block index: a decode write
+  // phase (4 rows x the 4 blocks, same chunk) then covers all 64 banks once,
+  // and a transposed read phase (4 rows x 4 aligned chunks of one block) still does.
+  auto w_slot = [](int row, int c) { return row * kBwRow + (c ^ ((c >> 3) & 3)); };
 
   f32x16 acc[4][4];
 #pragma unroll
