@@ -20,7 +20,9 @@ format (0.515869 bytes/param) written for the quantize, and per matmul the store
 (0.515869 bytes/param), the adapters and the activations in and out.
 
 Other shapes (--config 7b_mlp_up, 65b_up, ...) run the MFMA-bound training
-path (forward + backward dX at M = 4096 / 2048) and report TFLOP/s.
+path (forward + backward dX at M = 4096 / 2048) and report TFLOP/s;
+--config 7b_stack runs the whole 7B-shaped stack resident in HBM (224 fused
+forwards, then 224 fused backward dX, at M = 4096) and reports TFLOP/s.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 """
@@ -45,7 +47,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--config", default="7b_attn")
+    p.add_argument("--config", default="7b_attn",
+                   help="tiny, 7b_attn, 7b_mlp_up, 7b_mlp_down, 65b_up, 65b_attn or 7b_stack")
     p.add_argument("--copies", type=int, default=0, help="weight copies rotated (0 = auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle CPU time")
@@ -145,12 +148,112 @@ class Workload:
             wk[f"bwd_M{M}"] = (matmul_bytes(M, N, K, r, 1), matmul_flops(M, N, K, r))
         return wk
 
+    def step_work(self):
+        """(bytes, flops) of one step: every call once."""
+        wk = self.work()
+        return sum(b for b, _ in wk.values()), sum(f for _, f in wk.values())
+
+    def timing_groups(self):
+        """(label, launches) for per-call timing: one graph runs the call once per
+        weight copy of the rotation, C launches back to back."""
+        labels = [lab for lab, _ in self.calls(0)]
+        return [(lab, [self.calls(c)[i][1] for c in range(self.C)]) for i, lab in enumerate(labels)]
+
+    def describe(self):
+        shapes = {"7b_attn": "7B attention projection W 4096x4096", "7b_mlp_up": "7B MLP up W 11008x4096",
+                  "7b_mlp_down": "7B MLP down W 4096x11008", "65b_up": "65B up W 22016x8192",
+                  "65b_attn": "65B attention W 8192x8192", "tiny": "tiny W 256x256"}
+        return (f"{shapes.get(self.name, self.name)} NF4 blk64 + int8 double-quant (blk256), "
+                f"LoRA r={self.r} alpha={self.alpha:g}; step = quantize+DQ, fused fwd at "
+                f"M={','.join(map(str, self.Ms))}, fused bwd dX at M={self.bwd_M[0]}")
+
+    def config_extra(self):
+        return {"N": self.N, "K": self.K, "weight_copies_rotated": self.C}
+
+
+class StackWorkload:
+    """The 7B-shaped frozen stack: 32 layers x {q, k, v, o 4096x4096; gate, up
+    11008x4096; down 4096x11008}, every linear quantized (NF4 + double quant)
+    and resident in HBM, LoRA r=16 (alpha 32) on all 224 linears. One step runs
+    the 224 fused forwards at M = 4096 in layer order, then the 224 fused
+    backward dX in reverse order. Each linear has its own synthetic x and dY
+    (no attention, norms or activation functions between the linears); outputs
+    of equal shape share a buffer. W, adapters and activations are drawn on the
+    device from the per-linear seeds, W is quantized once before timing and its
+    fp32 copy freed."""
+
+    name = "7b_stack"
+
+    def __init__(self):
+        import torch
+        import synth
+        from qlora_dequant_gemm_amd import ops
+        self.torch, self.ops, self.synth = torch, ops, synth
+        self.L, self.lin = synth.STACK_LAYERS, synth.STACK_LINEARS
+        self.M, self.r, self.alpha = synth.STACK_M, synth.STACK_R, synth.STACK_ALPHA
+        self.Ms, self.bwd_M, self.decode, self.C = [self.M], [self.M], False, 1
+        self.lay = []
+        for l in range(self.L):
+            row = []
+            for j in range(len(self.lin)):
+                d = synth.stack_linear_device(l, j, self.M)
+                d["qw"] = ops.quantize_weight(d.pop("w"))
+                row.append(d)
+            self.lay.append(row)
+        self.nf4_bytes = sum(d["qw"].nbytes for row in self.lay for d in row)
+        self.y = {N: torch.empty((self.M, N), dtype=torch.bfloat16, device="cuda") for _, N, _ in self.lin}
+        self.dx = {K: torch.empty((self.M, K), dtype=torch.bfloat16, device="cuda") for _, _, K in self.lin}
+        self.ws = ops.Workspace("cuda")
+        self.ws.get(max(ops.workspace_bytes(op, self.M, N, K, self.r) for op in (0, 1) for _, N, K in self.lin))
+        torch.cuda.synchronize()
+
+    def _fwd(self, l, j):
+        d, N = self.lay[l][j], self.lin[j][1]
+        return lambda: self.ops.lora_fwd(d["x"], d["qw"], d["A"], d["B"], self.alpha, out=self.y[N], ws=self.ws)
+
+    def _bwd(self, l, j):
+        d, K = self.lay[l][j], self.lin[j][2]
+        return lambda: self.ops.bwd_dx(d["dy"], d["qw"], d["A"], d["B"], self.alpha, out=self.dx[K], ws=self.ws)
+
+    def calls(self, step):
+        nl = len(self.lin)
+        out = [(f"fwd_{self.lin[j][0]}", self._fwd(l, j)) for l in range(self.L) for j in range(nl)]
+        out += [(f"bwd_{self.lin[j][0]}", self._bwd(l, j)) for l in reversed(range(self.L))
+                for j in reversed(range(nl))]
+        return out
+
+    def timing_groups(self):
+        """(label, launches): one graph runs that linear's call in all 32 layers."""
+        nl = len(self.lin)
+        return ([(f"fwd_{self.lin[j][0]}", [self._fwd(l, j) for l in range(self.L)]) for j in range(nl)] +
+                [(f"bwd_{self.lin[j][0]}", [self._bwd(l, j) for l in range(self.L)]) for j in range(nl)])
+
+    def work(self):
+        wk = {}
+        for name, N, K in self.lin:
+            wk[f"fwd_{name}"] = (matmul_bytes(self.M, N, K, self.r, 0), matmul_flops(self.M, N, K, self.r))
+            wk[f"bwd_{name}"] = (matmul_bytes(self.M, N, K, self.r, 1), matmul_flops(self.M, N, K, self.r))
+        return wk
+
+    def step_work(self):
+        wk = self.work()
+        return (self.L * sum(b for b, _ in wk.values()), self.L * sum(f for _, f in wk.values()))
+
+    def describe(self):
+        return (f"7B-shaped frozen stack: {self.L} layers x {{q,k,v,o 4096x4096; gate,up 11008x4096; "
+                f"down 4096x11008}}, NF4 blk64 + int8 double-quant (blk256) resident in HBM "
+                f"({self.nf4_bytes} B), LoRA r={self.r} alpha={self.alpha:g} on all "
+                f"{self.L * len(self.lin)} linears; step = {self.L * len(self.lin)} fused fwd at M={self.M} "
+                f"in layer order, then {self.L * len(self.lin)} fused bwd dX in reverse")
+
+    def config_extra(self):
+        return {"layers": self.L, "linears": [list(t) for t in self.lin], "nf4_resident_bytes": self.nf4_bytes}
+
 
 def run_gpu(args):
     """Step time and per-call times, both from graph replays timed with events."""
     import torch
-    wl = Workload(args.config, args.copies)
-    labels = [lab for lab, _ in wl.calls(0)]
+    wl = StackWorkload() if args.config == "7b_stack" else Workload(args.config, args.copies)
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
@@ -185,16 +288,17 @@ def run_gpu(args):
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(end) / args.steps
 
-    # per-call durations: for each call, one graph runs it once per weight copy
-    # of the rotation (C launches back to back, each on a different copy);
-    # events on the launch stream bracket `reps` replays of that graph
+    # per-call durations: for each call, one graph runs its launches back to
+    # back (single matrix: once per weight copy of the rotation; stack: that
+    # linear in every layer); events on the launch stream bracket `reps`
+    # replays of that graph
     per_call = {}
-    reps = max(2, args.steps // wl.C)
-    for i, lab in enumerate(labels):
+    for lab, fns in wl.timing_groups():
+        reps = max(2, args.steps // len(fns))
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            for c in range(wl.C):
-                wl.calls(c)[i][1]()
+            for fn in fns:
+                fn()
         g.replay()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -205,7 +309,7 @@ def run_gpu(args):
                 g.replay()
             e1.record(stream)
         torch.cuda.synchronize()
-        per_call[lab] = e0.elapsed_time(e1) / (reps * wl.C)
+        per_call[lab] = e0.elapsed_time(e1) / (reps * len(fns))
     return wl, ms_step, per_call, wall
 
 
@@ -232,7 +336,7 @@ def cpu_baseline(args, wl):
     A, B = synth.adapters(N, K, r, s["A"], s["B"])
     xs = {M: synth.activations(M, K, s["x"]) for M in wl.Ms}
     dys = {M: synth.activations(M, N, s["dy"]) for M in wl.bwd_M}
-    step_bytes = sum(b for b, _ in wl.work().values())
+    step_bytes = wl.step_work()[0]
     rows = min(N, 256)                      # multiple of 4: 1024 weights = whole DQ groups
     done_rows = 0
     t_total = 0.0
@@ -262,6 +366,53 @@ def cpu_baseline(args, wl):
                       f"step's algorithmic bytes"}
 
 
+def cpu_baseline_stack(args, wl):
+    """The oracle on row slices of layer 0's q (4096x4096), gate (11008x4096)
+    and down (4096x11008), taken in turn: quantize + DQ + dequant of the slice,
+    then the fp64 forward and backward dX at M = 4096 against it. A slice of
+    rows is a smaller instance of the same per-row work; the rate is the
+    algorithmic flops done per second, the step's unit."""
+    import synth
+    import torch
+    from oracle import gemm, nf4
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+    host = []
+    for j in (0, 4, 6):
+        d = synth.stack_linear_device(0, j, wl.M)
+        host.append(dict(w=d["w"].cpu().numpy(), A=bits(d["A"]), B=bits(d["B"]), x=bits(d["x"]),
+                         dy=bits(d["dy"])))
+        del d
+    torch.cuda.empty_cache()
+    rows, M, r, alpha = 256, wl.M, wl.r, wl.alpha
+    flops = 0.0
+    t_total = 0.0
+    passes = 0
+    while t_total < args.cpu_seconds and t_total < 120.0:
+        h = host[passes % 3]
+        N, K = h["w"].shape
+        n0 = (passes // 3 * rows) % N
+        sl = slice(n0, min(N, n0 + rows))
+        nrow = sl.stop - sl.start
+        t = time.perf_counter()
+        packed, q, step, _ = nf4.quantize_all(h["w"][sl])
+        wd = nf4.dequantize(packed, q, step).reshape(nrow, K)
+        gemm.lora_forward(h["x"], wd, h["A"], h["B"][sl], alpha, r)
+        gemm.backward_dx(h["dy"][:, sl], wd, h["A"], h["B"][sl], alpha, r)
+        t_total += time.perf_counter() - t
+        flops += 2 * matmul_flops(M, nrow, K, r)
+        passes += 1
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(max(1, blas_threads)),
+            "host_cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{passes} oracle passes over {rows}-row slices of layer 0's q, gate and down in turn: "
+                      f"quantize + double-quant + dequant (numpy, one thread), fp64 forward and backward dX "
+                      f"at M={M} ({blas_threads} BLAS threads); {t_total:.1f} s, {flops / 1e12:.2f} TFLOP"}
+
+
 # ---------------------------------------------------------------------------
 # HBM traffic of the dominant kernel, from committed counter summaries
 # ---------------------------------------------------------------------------
@@ -273,7 +424,7 @@ CALL_KERNEL = {"quantize_dq": ("k_quantize", "quant.hip"), "fwd": ("k_gemv_fwd",
 
 
 def kernel_of(label, M):
-    key = label.split("_M")[0]
+    key = label if label == "quantize_dq" else label.split("_")[0]
     if key in ("fwd", "bwd") and M > 16:
         key += "_big"
     return CALL_KERNEL[key]
@@ -340,8 +491,7 @@ def main():
         return
     wl, ms_step, per_call, wall = run_gpu(args)
     wk = wl.work()
-    step_bytes = sum(b for b, _ in wk.values())
-    step_flops = sum(f for _, f in wk.values())
+    step_bytes, step_flops = wl.step_work()
     kernels = {}
     for lab, ms in per_call.items():
         b, f = wk[lab]
@@ -363,34 +513,32 @@ def main():
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": round(ach / MFMA_BF16_PEAK_TFS, 4), "traffic": traffic, "kernel": kname, "call": dom,
                 "algorithmic_flops": f, "ms": round(per_call[dom], 5)}
+    metric = "fused NF4-dequant GEMM TFLOP/s + weight-stream GB/s (% of MI355X roofline)"
     if wl.decode:
-        metric = "fused NF4-dequant GEMM TFLOP/s + weight-stream GB/s (% of MI355X roofline)"
         value, unit = step_bytes / ms_step / 1e6, "GB/s"
     else:
-        metric = "fused NF4-dequant GEMM TFLOP/s + weight-stream GB/s (% of MI355X roofline)"
         value, unit = step_flops / ms_step / 1e9, "TFLOP/s"
-    shapes = {"7b_attn": "7B attention projection W 4096x4096", "7b_mlp_up": "7B MLP up W 11008x4096",
-              "7b_mlp_down": "7B MLP down W 4096x11008", "65b_up": "65B up W 22016x8192",
-              "65b_attn": "65B attention W 8192x8192", "tiny": "tiny W 256x256"}
+    config = {"workload": wl.describe(), "name": wl.name, "M": wl.Ms, "r": wl.r, "alpha": wl.alpha,
+              "parallelism": "single GPU"}
+    config.update(wl.config_extra())
     line = {
         "metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{shapes.get(wl.name, wl.name)} NF4 blk64 + int8 double-quant (blk256), "
-                               f"LoRA r={wl.r} alpha={wl.alpha:g}; step = quantize+DQ, fused fwd at "
-                               f"M={','.join(map(str, wl.Ms))}, fused bwd dX at M={wl.bwd_M[0]}",
-                   "name": wl.name, "N": wl.N, "K": wl.K, "M": wl.Ms, "r": wl.r, "alpha": wl.alpha,
-                   "weight_copies_rotated": wl.C, "parallelism": "single GPU"},
+        "config": config,
         "roofline": roof,
         "kernels": kernels,
         "step_bytes": step_bytes, "step_flops": step_flops,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args, wl)
-        if unit == "TFLOP/s":
-            cb = line["cpu_baseline"]
-            cb["value"] = cb["value"] * step_flops / step_bytes / 1e3
-            cb["unit"] = "TFLOP/s"
+        if isinstance(wl, StackWorkload):
+            line["cpu_baseline"] = cpu_baseline_stack(args, wl)
+        else:
+            line["cpu_baseline"] = cpu_baseline(args, wl)
+            if unit == "TFLOP/s":
+                cb = line["cpu_baseline"]
+                cb["value"] = cb["value"] * step_flops / step_bytes / 1e3
+                cb["unit"] = "TFLOP/s"
     print(json.dumps(line), flush=True)
 
 

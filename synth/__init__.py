@@ -41,6 +41,7 @@ STACK_LINEARS = [("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096),
                  ("o", 4096, 4096), ("gate", 11008, 4096),
                  ("up", 11008, 4096), ("down", 4096, 11008)]
 STACK_LAYERS = 32
+STACK_M, STACK_R, STACK_ALPHA = 4096, 16, 32.0
 
 
 def _rng(seed):
@@ -97,3 +98,27 @@ def config_inputs(name, M=None):
 
 def stack_seed(layer, j):
     return 1000 + 10 * layer + j
+
+
+def stack_linear_device(layer, j, M=STACK_M, device="cuda", acts=True):
+    """Inputs of linear j of layer `layer` of the 7B-shaped stack, drawn on the
+    device by torch's generator seeded with stack_seed(layer, j), in the order
+    W, A, B, x, dY (so W alone can be drawn again from the same seed):
+    W fp32 [N, K] ~ N(0, 0.02); A [r, K], B [N, r] ~ N(0, 0.01), x [M, K] and
+    dY [M, N] ~ N(0, 1), all four rounded to bf16. Returns a dict of device
+    tensors: x and dY are left out when acts is False, and everything but W
+    when acts is None."""
+    import torch
+    _, N, K = STACK_LINEARS[j]
+    g = torch.Generator(device=device)
+    g.manual_seed(stack_seed(layer, j))
+    draw = lambda shape: torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    out = {"w": draw((N, K)) * WEIGHT_STD}
+    if acts is None:
+        return out
+    out["A"] = (draw((STACK_R, K)) * ADAPTER_STD).to(torch.bfloat16)
+    out["B"] = (draw((N, STACK_R)) * ADAPTER_STD).to(torch.bfloat16)
+    if acts:
+        out["x"] = draw((M, K)).to(torch.bfloat16)
+        out["dy"] = draw((M, N)).to(torch.bfloat16)
+    return out

@@ -400,3 +400,88 @@ def test_full_size_every_output(qops, name):
     assert _elementwise_ok(d1.float(), ref, S, T, scale) == 0
     del qw, wd
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# the whole 7B-shaped stack, resident in HBM
+# ---------------------------------------------------------------------------
+def test_stack_resident_step(qops):
+    """All 224 linears (32 layers x q, k, v, o, gate, up, down) quantized and
+    resident together, then one step as the benchmark runs it: 224 forwards in
+    layer order, 224 backward dX in reverse, outputs of equal shape sharing a
+    buffer, one workspace. Checks: the resident format is the storage rate
+    times the stack's parameter count (3,340,771,328 bytes); sampled DQ groups
+    of every linear of layers 0 and 31 are bit-exact against the oracle; the
+    outputs left by the last forward (layer 31 down) and the last backward
+    (layer 0 q) match the oracle on sampled entries and equal the same calls
+    made alone."""
+    from oracle import storage
+    L, lin, M = synth.STACK_LAYERS, synth.STACK_LINEARS, synth.STACK_M
+    r, alpha = synth.STACK_R, synth.STACK_ALPHA
+    lay = []
+    for l in range(L):
+        row = []
+        for j in range(len(lin)):
+            d = synth.stack_linear_device(l, j, M, acts=(l, j) in ((L - 1, 6), (0, 0)))
+            d["qw"] = qops.quantize_weight(d.pop("w"))
+            row.append(d)
+        lay.append(row)
+    params = L * sum(N * K for _, N, K in lin)
+    resident = sum(d["qw"].nbytes for row in lay for d in row)
+    assert params == 6_476_005_376
+    assert resident == 3_340_771_328 == params * storage.bytes_per_param(1 << 16)
+
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    xs = {K: torch.randn((M, K), generator=gen, device="cuda").bfloat16() for K in (4096, 11008)}
+    dys = {N: torch.randn((M, N), generator=gen, device="cuda").bfloat16() for N in (4096, 11008)}
+    y = {N: torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for N in (4096, 11008)}
+    dx = {K: torch.empty((M, K), dtype=torch.bfloat16, device="cuda") for K in (4096, 11008)}
+    ws = qops.Workspace("cuda")
+    for l in range(L):
+        for j, (_, N, K) in enumerate(lin):
+            d = lay[l][j]
+            qops.lora_fwd(d.get("x", xs[K]), d["qw"], d["A"], d["B"], alpha, out=y[N], ws=ws)
+    for l in reversed(range(L)):
+        for j in reversed(range(len(lin))):
+            _, N, K = lin[j]
+            d = lay[l][j]
+            qops.bwd_dx(d.get("dy", dys[N]), d["qw"], d["A"], d["B"], alpha, out=dx[K], ws=ws)
+    torch.cuda.synchronize()
+    last_y, last_dx = y[4096].clone(), dx[4096].clone()
+    top, bot = lay[L - 1][6], lay[0][0]
+    assert torch.equal(qops.lora_fwd(top["x"], top["qw"], top["A"], top["B"], alpha), last_y)
+    assert torch.equal(qops.bwd_dx(bot["dy"], bot["qw"], bot["A"], bot["B"], alpha), last_dx)
+
+    rng = np.random.Generator(np.random.PCG64(11))
+    for l in (0, L - 1):
+        for j, (_, N, K) in enumerate(lin):
+            w = synth.stack_linear_device(l, j, M, acts=None)["w"].cpu().numpy().reshape(-1)
+            qw = lay[l][j]["qw"]
+            packed, q, step = qw.packed.cpu().numpy(), qw.qscale.cpu().numpy(), qw.step.cpu().numpy()
+            for g in sorted(rng.choice(step.size, 8, replace=False)):
+                lo, hi = g * 16384, (g + 1) * 16384
+                opk, oa = nf4.quantize(w[lo:hi])
+                oq, ostep = nf4.double_quantize(oa)
+                assert np.array_equal(packed[lo // 2:hi // 2], opk), (l, j, g)
+                assert np.array_equal(q[lo // 64:hi // 64], oq), (l, j, g)
+                assert step[g].view(np.uint32) == ostep[0].view(np.uint32), (l, j, g)
+
+    bits = host_bits
+    for d, (l, j), out, fwd in ((top, (L - 1, 6), last_y, True), (bot, (0, 0), last_dx, False)):
+        _, N, K = lin[j]
+        w = synth.stack_linear_device(l, j, M, acts=None)["w"].cpu().numpy()
+        opk, oq, ostep, _ = nf4.quantize_all(w)
+        wd = nf4.dequantize(opk, oq, ostep).reshape(N, K)
+        A, B, got = bits(d["A"]), bits(d["B"]), bits(out)
+        ms = rng.integers(0, M, 64)
+        if fwd:
+            ns = rng.integers(0, N, 64)
+            ref = gemm.lora_forward_at(ms, ns, bits(d["x"]), lambda n: wd[int(n)], A, B, alpha, r)
+            assert rel_fro(to_f64(got[ms, ns]), ref) <= TIGHT
+        else:
+            ks = rng.integers(0, K, 64)
+            ref = gemm.backward_dx_at(ms, ks, bits(d["dy"]), lambda k: wd[:, int(k)], A, B, alpha, r)
+            assert rel_fro(to_f64(got[ms, ks]), ref) <= TIGHT
+    del lay, xs, dys, y, dx
+    torch.cuda.empty_cache()
