@@ -15,11 +15,19 @@ Sources, cited by page title and section:
   [STEP]      "QLoRA" (techbytebybyte), section "Follow one QLoRA training
               step": gradients go into the adapters, not the frozen base.
 
+  [BASE]      "QLoRA Explained: ...", "What is QLoRA?" (the base is frozen:
+              gradients and optimizer state exist only for the adapters);
+              "QLoRA and Quantized Training", "The idea" (the adapters hold
+              the gradients and optimizer state, in bf16).
+
 Definitions (the LoRA scale alpha/r is the standard one for these knobs):
   forward   y  = x . W'^T + (alpha/r) . (x . A^T) . B^T
   backward  dX = dY . W'  [+ (alpha/r) . (dY . B) . A]
+  adapters  dB = (alpha/r) . dY^T . (x . A^T)      [N, r]
+            dA = (alpha/r) . (dY . B)^T . x        [r, K]
 with W' [N,K] the dequantized bf16 weight, x [M,K], A [r,K], B [N,r],
-dY [M,N]. Inputs are bf16 bit patterns (uint16); the products are taken in
+dY [M,N]. The adapter gradients are those of the scalar <dY, y> with respect
+to B and A: y is linear in each adapter with the other held fixed. Inputs are bf16 bit patterns (uint16); the products are taken in
 fp64 on the exact bf16 values, which is the real-number result the bf16
 kernels approximate. r == 0 means no adapter.
 """
@@ -91,3 +99,19 @@ def backward_dx_at(ms, ks, dy_bits, wcol, A_bits=None, B_bits=None, alpha=0.0, r
             acc += (alpha / r) * float(np.dot(dy[m] @ B, A[:, k]))
         out[i] = acc
     return out
+
+
+def lora_grads(x_bits, dy_bits, A_bits, B_bits, alpha, r):
+    """(dA [r,K], dB [N,r]) in fp64 ([ARCH-fig2], [STEP], [BASE]).
+
+    With s = alpha/r, t = x . A^T and u = dY . B (exact, no rounding):
+    dB = s . dY^T . t and dA = s . u^T . x.
+    """
+    x = bf16_to_f64(x_bits)
+    dy = bf16_to_f64(dy_bits)
+    A = bf16_to_f64(A_bits)
+    B = bf16_to_f64(B_bits)
+    s = alpha / r
+    t = x @ A.T
+    u = dy @ B
+    return s * (u.T @ x), s * (dy.T @ t)

@@ -8,6 +8,9 @@ Training", "In code" (r, lora_alpha).
 Pins used: one-hot inputs (a single product per output), the adjoint identity
 <fwd(x), dY> = <x, bwd(dY)> that fixes every transposition, a closed-form
 rank-one adapter, linearity, and a pure-Python scalar loop on a tiny case.
+Adapter gradients: directional derivatives taken through the forward itself
+(y is linear in each adapter), torch autograd in fp64, and a one-hot closed
+form.
 """
 import math
 
@@ -121,3 +124,64 @@ def test_sampled_entries_equal_full_products():
     ds = gemm.backward_dx_at(ms, ks, dy, lambda k: wd[:, k], A, B, 4.0, r)
     assert np.allclose(ys, y[ms, ns], rtol=1e-12, atol=1e-12)
     assert np.allclose(ds, dx[ms, ks], rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# adapter gradients dA, dB (the gradients of <dY, y> with respect to A and B)
+# ---------------------------------------------------------------------------
+def test_adapter_grads_directional_derivatives_through_forward():
+    """y is linear in B with A fixed and in A with B fixed, so for any
+    direction E of B and F of A the forward itself (weight zero) gives
+    <dY, fwd(x; A, E)> = <dB, E> and <dY, fwd(x; F, B)> = <dA, F>. Shapes
+    are all distinct, so a transposed or swapped gradient cannot pass."""
+    M, N, K, r = 9, 40, 192, 5
+    _, x, A, B, dy = _setup(M, N, K, r, 300)
+    alpha = 7.0
+    dA, dB = gemm.lora_grads(x, dy, A, B, alpha, r)
+    assert dA.shape == (r, K) and dB.shape == (N, r)
+    zero_n = np.zeros((N, K), np.uint16)
+    dyf = gemm.bf16_to_f64(dy)
+    rng = np.random.Generator(np.random.PCG64(301))
+    for _ in range(3):
+        E = _bits(rng.standard_normal((N, r)).astype(np.float32))
+        F = _bits(rng.standard_normal((r, K)).astype(np.float32))
+        lb = np.sum(dyf * gemm.lora_forward(x, zero_n, A, E, alpha, r))
+        la = np.sum(dyf * gemm.lora_forward(x, zero_n, F, B, alpha, r))
+        ib = np.sum(dB * gemm.bf16_to_f64(E))
+        ia = np.sum(dA * gemm.bf16_to_f64(F))
+        assert abs(lb - ib) <= 1e-10 * (abs(lb) + 1)
+        assert abs(la - ia) <= 1e-10 * (abs(la) + 1)
+
+
+def test_adapter_grads_match_autograd():
+    """torch autograd (CPU, fp64) of <dY, x W'^T + s (x A^T) B^T> with respect to
+    A and B: an independent derivation of the same gradients."""
+    import torch
+    M, N, K, r = 13, 24, 128, 8
+    wd, x, A, B, dy = _setup(M, N, K, r, 310)
+    alpha = 16.0
+    dA, dB = gemm.lora_grads(x, dy, A, B, alpha, r)
+    T = lambda a: torch.from_numpy(gemm.bf16_to_f64(a))
+    xt, wt, dyt = T(x), T(wd), T(dy)
+    At, Bt = T(A).requires_grad_(), T(B).requires_grad_()
+    y = xt @ wt.T + (alpha / r) * (xt @ At.T) @ Bt.T
+    (y * dyt).sum().backward()
+    assert np.allclose(dA, At.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(dB, Bt.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_adapter_grads_one_hot_closed_form():
+    """x = e_k in row m, dY = e_n in row m: dB[n, :] = s A[:, k] and
+    dA[:, k] = s B[n, :], everything else zero (single products, exact)."""
+    M, N, K, r = 3, 16, 64, 4
+    _, _, A, B, _ = _setup(1, N, K, r, 320)
+    x = np.zeros((M, K), np.float32)
+    dy = np.zeros((M, N), np.float32)
+    x[1, 37] = 1.0
+    dy[1, 5] = 1.0
+    dA, dB = gemm.lora_grads(_bits(x), _bits(dy), A, B, 8.0, r)
+    eA = np.zeros((r, K))
+    eB = np.zeros((N, r))
+    eB[5] = 2.0 * gemm.bf16_to_f64(A)[:, 37]
+    eA[:, 37] = 2.0 * gemm.bf16_to_f64(B)[5]
+    assert np.array_equal(dA, eA) and np.array_equal(dB, eB)
