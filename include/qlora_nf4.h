@@ -123,9 +123,10 @@ int qlora_nf4_dequant(const uint8_t* packed, const int8_t* qscale,
                       void* stream);
 
 /*
- * Workspace (device bytes) that qlora_nf4_lora_fwd (op = 0) or
- * qlora_nf4_bwd_dx (op = 1) needs for these sizes; 0 when none is needed.
- * Returns 0 for invalid sizes as well (the call itself reports the error).
+ * Workspace (device bytes) that qlora_nf4_lora_fwd (op = 0),
+ * qlora_nf4_bwd_dx (op = 1) or qlora_lora_grad (op = 2) needs for these
+ * sizes; 0 when none is needed. Returns 0 for invalid sizes as well (the call
+ * itself reports the error).
  */
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r);
 
@@ -169,6 +170,36 @@ int qlora_nf4_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K,
                      const float* step, const uint16_t* A, const uint16_t* B,
                      int r, float alpha, uint16_t* dx, void* workspace,
                      size_t ws_bytes, void* stream);
+
+/*
+ * Gradients of the LoRA adapters of one QLoRA linear, the only trainable
+ * parameters: the base weight is frozen and gradients and optimizer state
+ * exist for the adapters alone ("QLoRA Explained", "What is QLoRA?"; "QLoRA
+ * and Quantized Training", "The idea"; figure 2 of "A 65B fine-tune on the GPU
+ * you already have"). They are those of the scalar <dY, y> for the forward
+ * above, with s = alpha / r:
+ *     dB = s . dY^T . t,  t = bf16(x . A^T)      [N, r]
+ *     dA = s . u^T . x,   u = bf16(dY . B)       [r, K]
+ * (t and u are the bf16 values the fused forward and backward use.)
+ *   x       [M, K] bf16, the layer input of the forward; M >= 1, K multiple
+ *           of 64.
+ *   dy      [M, N] bf16, the gradient of y; N >= 1 multiple of 8.
+ *   A, B    [r, K] and [N, r] bf16 adapters, 1 <= r <= 128; alpha as in the
+ *           forward.
+ *   dA, dB  [r, K] and [N, r] fp32 out (the layouts of A and B). accumulate
+ *           = 0 overwrites them, 1 adds the gradients to what they hold
+ *           (accumulation over micro-batches).
+ *   workspace / ws_bytes  at least qlora_workspace_bytes(2, M, N, K, r).
+ * Products are bf16 x bf16 accumulated in fp32; the result does not depend
+ * on scheduling (partial sums are added in a fixed order). Every pointer must
+ * be 16-byte aligned. The weight itself is not an argument: neither gradient
+ * depends on it.
+ */
+int qlora_lora_grad(const uint16_t* x, const uint16_t* dy, int64_t M,
+                    int64_t N, int64_t K, const uint16_t* A,
+                    const uint16_t* B, int r, float alpha, float* dA,
+                    float* dB, int accumulate, void* workspace,
+                    size_t ws_bytes, void* stream);
 
 /*
  * Host copy of the 16 fp32 levels and the 15 fp32 decision thresholds the

@@ -77,7 +77,8 @@ int qlora_nf4_codebook(float levels[16], float thresholds[15]) {
 }
 
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r) {
-  if ((op != 0 && op != 1) || M < 1 || N < 1 || K < 64 || r < 0 || r > QLORA_MAX_RANK) return 0;
+  if (op < 0 || op > 2 || M < 1 || N < 1 || K < 64 || r < 0 || r > QLORA_MAX_RANK) return 0;
+  if (op == 2) return r > 0 ? qnf4::grad_plan(M, N, K, r).total : 0;
   return qnf4::ws_layout(op, M, N, K, r).total;
 }
 
@@ -156,6 +157,23 @@ int qlora_nf4_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K, const 
   if (!cb) return QLORA_ERR_INIT;
   return hip_status(qnf4::launch_bwd_dx(dy, M, N, K, packed, qscale, step, A, B, r, alpha, dx, workspace, *cb,
                                         as_stream(stream)));
+}
+
+int qlora_lora_grad(const uint16_t* x, const uint16_t* dy, int64_t M, int64_t N, int64_t K, const uint16_t* A,
+                    const uint16_t* B, int r, float alpha, float* dA, float* dB, int accumulate, void* workspace,
+                    size_t ws_bytes, void* stream) {
+  if (!x || !dy || !dA || !dB) return QLORA_ERR_NULL;
+  if (M < 1 || N < 1 || N % 8 != 0 || K < 64 || K % QLORA_BLOCK != 0) return QLORA_ERR_SHAPE;
+  if (M > (int64_t{1} << 31) || N > (int64_t{1} << 31) || K > (int64_t{1} << 31)) return QLORA_ERR_SHAPE;
+  if (r < 1 || r > QLORA_MAX_RANK) return QLORA_ERR_RANK;
+  if (!A || !B) return QLORA_ERR_NULL;
+  if (accumulate != 0 && accumulate != 1) return QLORA_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(A) || !aligned16(B) || !aligned16(dA) || !aligned16(dB))
+    return QLORA_ERR_ALIGN;
+  const int st = check_ws(workspace, ws_bytes, qnf4::grad_plan(M, N, K, r).total);
+  if (st) return st;
+  return hip_status(qnf4::launch_lora_grad(x, dy, M, N, K, A, B, r, alpha, dA, dB, accumulate, workspace,
+                                           as_stream(stream)));
 }
 
 }  // extern "C"

@@ -69,6 +69,14 @@ inline WsLayout ws_layout(int op, int64_t M, int64_t N, int64_t K, int r) {
   return w;
 }
 
+// Adapter gradients (dA, dB): workspace plan. Mp = M rounded up to 64 (rows of
+// the transposed t and u); SB / SA = row splits of the dY and x contractions.
+struct GradPlan {
+  int64_t Mp = 0, rp = 0, SB = 1, SA = 1;
+  size_t bt_off = 0, tt_off = 0, ut_off = 0, pb_off = 0, pa_off = 0, total = 0;
+};
+GradPlan grad_plan(int64_t M, int64_t N, int64_t K, int r);
+
 // qscale/step may be NULL (quantize only); otherwise the constants are also
 // double-quantized in the same pass.
 hipError_t launch_quantize(const void* w, int wdt, int64_t numel, uint8_t* packed, float* absmax,
@@ -79,10 +87,12 @@ hipError_t launch_dequant(const uint8_t* packed, const int8_t* qscale, const flo
                           uint16_t* out, const Codebook& cb, hipStream_t stream);
 
 // rank-r down projection of `in` [M][Kc] by the adapter (wrow: A [r][Kc];
-// else B [Kc][r]); M <= kSmallM writes lora_splits fp32 partials, else bf16.
-// wt: workspace for the transposed adapter (large M, wrow == false; r * Kc bf16)
+// else B [Kc][r]); M <= kSmallM writes lora_splits fp32 partials, else bf16
+// [M][rp]. ldt > 0: bf16 transposed, out [rp][ldt] (ldt a multiple of 16, >= M,
+// rows past M zero), for any M.
+// wt: workspace for the transposed adapter (bf16 path, wrow == false; r * Kc bf16)
 hipError_t launch_lora_down(bool wrow, const uint16_t* in, int64_t M, int64_t Kc, const uint16_t* W, int r,
-                            void* out, hipStream_t stream, uint16_t* wt);
+                            void* out, hipStream_t stream, uint16_t* wt, int64_t ldt = 0);
 hipError_t launch_fwd_small(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
                             const int8_t* qscale, const float* step, const float* tpart, int St, int rp,
                             const uint16_t* B, int r, float scale, uint16_t* y, const Codebook& cb,
@@ -100,5 +110,8 @@ hipError_t launch_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K, co
                          const int8_t* qscale, const float* step, const uint16_t* A, const uint16_t* B,
                          int r, float alpha, uint16_t* dx, void* ws, const Codebook& cb,
                          hipStream_t stream);
+hipError_t launch_lora_grad(const uint16_t* x, const uint16_t* dy, int64_t M, int64_t N, int64_t K,
+                            const uint16_t* A, const uint16_t* B, int r, float alpha, float* dA, float* dB,
+                            int accumulate, void* ws, hipStream_t stream);
 
 }  // namespace qnf4

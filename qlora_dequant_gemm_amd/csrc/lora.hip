@@ -35,13 +35,15 @@ __device__ __forceinline__ u32x4 adapter8(const uint16_t* __restrict__ W, int64_
 // from global memory; the adapter stays in L2), then reduce through LDS.
 // ---------------------------------------------------------------------------
 // NT: 16-wide rank tiles holding real ranks (ceil(r / 16)); the padding
-// columns up to rp are written as zero. Each wave takes 32-deep contraction
+// columns up to rp are written as zero. TRANS writes the result transposed,
+// out [rp][ldt] with ldt >= M, rows m in [M, ldt) zero (the grid then covers
+// ldt / 16 row tiles). Each wave takes 32-deep contraction
 // steps round robin in groups of 8, all of a group's loads issued before its
 // MFMAs, so that enough loads are in flight to stream `in` from HBM.
-template <int NT>
+template <int NT, bool TRANS>
 __global__ __launch_bounds__(256) void k_lora_down(const uint16_t* __restrict__ in, int64_t M, int64_t Kc,
                                                    const uint16_t* __restrict__ W, int r, int rp,
-                                                   uint16_t* __restrict__ out) {
+                                                   uint16_t* __restrict__ out, int64_t ldt) {
   __shared__ f32x4 red[4][8][64];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -78,7 +80,11 @@ __global__ __launch_bounds__(256) void k_lora_down(const uint16_t* __restrict__ 
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int64_t m = m0 + 4 * (ln >> 4) + v;
-      if (m < M) out[m * rp + 16 * jt + (ln & 15)] = bf16_bits(sum[v]);
+      if (TRANS) {
+        if (m < ldt) out[(16 * jt + (ln & 15)) * ldt + m] = m < M ? bf16_bits(sum[v]) : uint16_t{0};
+      } else if (m < M) {
+        out[m * rp + 16 * jt + (ln & 15)] = bf16_bits(sum[v]);
+      }
     }
   }
 }
@@ -138,9 +144,9 @@ __global__ __launch_bounds__(256) void k_adapter_t(const uint16_t* __restrict__ 
 }
 
 hipError_t launch_lora_down(bool wrow, const uint16_t* in, int64_t M, int64_t Kc, const uint16_t* W, int r,
-                            void* out, hipStream_t stream, uint16_t* wt) {
+                            void* out, hipStream_t stream, uint16_t* wt, int64_t ldt) {
   const int rp = static_cast<int>(rank_pad(r));
-  if (M <= kSmallM) {
+  if (M <= kSmallM && ldt == 0) {
     const int S = static_cast<int>(lora_splits(M, Kc));
     if (wrow)
       hipLaunchKernelGGL(k_lora_down_small<true>, dim3(S), dim3(512), 0, stream, in, M, Kc, W, r, rp, S,
@@ -149,7 +155,7 @@ hipError_t launch_lora_down(bool wrow, const uint16_t* in, int64_t M, int64_t Kc
       hipLaunchKernelGGL(k_lora_down_small<false>, dim3(S), dim3(512), 0, stream, in, M, Kc, W, r, rp, S,
                          static_cast<float*>(out));
   } else {
-    const unsigned grid = static_cast<unsigned>(cdiv(M, 16));
+    const unsigned grid = static_cast<unsigned>(cdiv(ldt ? ldt : M, 16));
     const uint16_t* Wr = W;
     if (!wrow) {
       hipLaunchKernelGGL(k_adapter_t, dim3(static_cast<unsigned>(cdiv(Kc, 256))), dim3(256), 0, stream, W, Kc, r,
@@ -157,9 +163,13 @@ hipError_t launch_lora_down(bool wrow, const uint16_t* in, int64_t M, int64_t Kc
       Wr = wt;
     }
     const int nt = (r + 15) / 16;
-#define QNF4_LDOWN(NTV)                                                                                   \
-  hipLaunchKernelGGL(k_lora_down<NTV>, dim3(grid), dim3(256), 0, stream, in, M, Kc, Wr, r, rp, \
-                     static_cast<uint16_t*>(out))
+#define QNF4_LDOWN(NTV)                                                                                     \
+  if (ldt)                                                                                                  \
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(k_lora_down<NTV, true>), dim3(grid), dim3(256), 0, stream, in, M, Kc, \
+                       Wr, r, rp, static_cast<uint16_t*>(out), ldt);                                        \
+  else                                                                                                      \
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(k_lora_down<NTV, false>), dim3(grid), dim3(256), 0, stream, in, M, Kc, \
+                       Wr, r, rp, static_cast<uint16_t*>(out), ldt)
     if (nt <= 1)
       QNF4_LDOWN(1);
     else if (nt == 2)

@@ -177,6 +177,33 @@ def bwd_dx(dy, qw, A=None, B=None, alpha=0.0, out=None, ws=None):
     return out
 
 
+def lora_grad(x, dy, A, B, alpha, dA=None, dB=None, accumulate=False, ws=None):
+    """Adapter gradients (dA [r, K], dB [N, r], fp32) of one QLoRA linear:
+    dB = (alpha/r) . dY^T . bf16(x . A^T), dA = (alpha/r) . bf16(dY . B)^T . x.
+    With accumulate=True they are added to dA and dB."""
+    _need(x, torch.bfloat16, "x")
+    _need(dy, torch.bfloat16, "dy")
+    _need(A, torch.bfloat16, "A")
+    _need(B, torch.bfloat16, "B")
+    M, K = x.shape
+    N = dy.shape[1]
+    r = A.shape[0]
+    if dy.shape[0] != M or A.shape[1] != K or tuple(B.shape) != (N, r):
+        raise ValueError("inconsistent shapes")
+    if dA is None:
+        dA = (torch.zeros if accumulate else torch.empty)((r, K), dtype=torch.float32, device=x.device)
+    if dB is None:
+        dB = (torch.zeros if accumulate else torch.empty)((N, r), dtype=torch.float32, device=x.device)
+    _need(dA, torch.float32, "dA")
+    _need(dB, torch.float32, "dB")
+    need = workspace_bytes(2, M, N, K, r)
+    wsb = (ws or Workspace(x.device)).get(need)
+    _lib.check("qlora_lora_grad", _lib.lib().qlora_lora_grad(
+        _ptr(x), _ptr(dy), M, N, K, _ptr(A), _ptr(B), r, float(alpha), _ptr(dA), _ptr(dB),
+        1 if accumulate else 0, _ptr(wsb), 0 if wsb is None else wsb.numel(), _stream(x.device)))
+    return dA, dB
+
+
 def codebook():
     """(levels[16], thresholds[15]) as the kernels use them, host floats."""
     L = (ctypes.c_float * 16)()

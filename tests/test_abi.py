@@ -58,8 +58,15 @@ def test_workspace_sizes():
     assert ws(1, 16, 4096, 4096, 0) > 0                           # small-M backward partials
     assert ws(1, 4096, 4096, 11008, 0) == 0
     assert ws(2, 16, 16, 64, 0) == 0 and ws(0, 0, 16, 64, 0) == 0
-    for op in (0, 1):
+    for op in (0, 1, 2):
         assert ws(op, 16, 8, 64, 8) % 256 == 0
+    # adapter gradients: transposed B, t^T and u^T (rank padded to 32, rows to
+    # 64), and the fp32 partials of the dY and x contractions
+    assert ws(3, 16, 16, 64, 8) == 0 and ws(2, 16, 16, 64, 129) == 0
+    g = ws(2, 4096, 11008, 4096, 16)
+    fixed = 16 * 11008 * 2 + 2 * 32 * 4096 * 2
+    assert g >= fixed + 11008 * 16 * 4 + 4096 * 16 * 4
+    assert g <= fixed + 64 * (11008 + 4096) * 16 * 4 + 5 * 256
 
 
 V = ctypes.c_void_p
@@ -102,6 +109,26 @@ def test_forward_rejects_bad_arguments(kwargs, status):
 ])
 def test_backward_rejects_bad_arguments(kwargs, status):
     assert _bwd(**kwargs) == status
+
+
+def _grad(x=FAKE, dy=FAKE, M=16, N=64, K=64, A=FAKE, B=FAKE, r=8, alpha=16.0, dA=FAKE, dB=FAKE, acc=0,
+          ws=None, wsb=None):
+    if wsb is None:
+        wsb = ops.workspace_bytes(2, M, N, K, r)
+        ws = FAKE if wsb else V(0)
+    return _lib.lib().qlora_lora_grad(x, dy, M, N, K, A, B, r, alpha, dA, dB, acc, ws, wsb, V(0))
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(x=V(0)), 1), (dict(dy=V(0)), 1), (dict(dA=V(0)), 1), (dict(dB=V(0)), 1),
+    (dict(A=V(0)), 1), (dict(B=V(0)), 1),
+    (dict(M=0), 2), (dict(N=12), 2), (dict(K=100), 2), (dict(acc=2), 2),
+    (dict(r=0), 4), (dict(r=129), 4),
+    (dict(x=ODD), 3), (dict(dy=ODD), 3), (dict(dA=ODD), 3), (dict(dB=ODD), 3), (dict(A=ODD), 3),
+    (dict(ws=V(0), wsb=0), 5), (dict(ws=FAKE, wsb=256), 5), (dict(ws=ODD, wsb=1 << 30), 3),
+])
+def test_adapter_grad_rejects_bad_arguments(kwargs, status):
+    assert _grad(**kwargs) == status
 
 
 def test_quantize_dq_dequant_reject_bad_arguments():

@@ -485,3 +485,96 @@ def test_stack_resident_step(qops):
             assert rel_fro(to_f64(got[ms, ks]), ref) <= TIGHT
     del lay, xs, dys, y, dx
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# adapter gradients dA, dB
+# ---------------------------------------------------------------------------
+GRAD_CASES = [
+    # M, N, K, r, alpha, seed
+    (16, 256, 256, 8, 16.0, 0),        # the tiny config
+    (1, 64, 64, 16, 32.0, 1),          # a single token
+    (5, 40, 64, 5, 7.0, 2),            # ragged column tile, odd rank
+    (300, 520, 320, 16, 32.0, 3),      # ragged M (not a multiple of the 64-row chunk) and N
+    (100, 48, 64, 32, 32.0, 4),        # two rank tiles
+    (513, 264, 128, 64, 16.0, 5),      # four rank tiles
+    (200, 136, 192, 128, 8.0, 6),      # the largest rank
+    (4096, 1024, 512, 16, 32.0, 7),    # many row splits of two chunks each
+]
+
+
+def _grad_case(ops, M, N, K, r, alpha, seed):
+    x = synth.activations(M, K, 400 + seed)
+    dy = synth.activations(M, N, 500 + seed)
+    A, B = synth.adapters(N, K, r, 600 + seed, 700 + seed)
+    dA, dB = ops.lora_grad(dev(x), dev(dy), dev(A), dev(B), alpha)
+    oA, oB = gemm.lora_grads(x, dy, A, B, alpha, r)
+    return dA.cpu().numpy().astype(np.float64), dB.cpu().numpy().astype(np.float64), oA, oB
+
+
+@pytest.mark.parametrize("M,N,K,r,alpha,seed", GRAD_CASES)
+def test_adapter_grad_parity(qops, M, N, K, r, alpha, seed):
+    gA, gB, oA, oB = _grad_case(qops, M, N, K, r, alpha, seed)
+    assert rel_fro(gA, oA) <= TIGHT and rel_fro(gB, oB) <= TIGHT
+
+
+def test_adapter_grad_accumulate_and_determinism(qops):
+    M, N, K, r, alpha = 300, 520, 320, 16, 32.0
+    x = dev(synth.activations(M, K, 410))
+    dy = dev(synth.activations(M, N, 510))
+    A, B = (dev(a) for a in synth.adapters(N, K, r, 610, 710))
+    dA1, dB1 = qops.lora_grad(x, dy, A, B, alpha)
+    dA2, dB2 = qops.lora_grad(x, dy, A, B, alpha)
+    assert torch.equal(dA1, dA2) and torch.equal(dB1, dB2)
+    # accumulate: the second call adds the same values, so the sum is exactly 2x
+    qops.lora_grad(x, dy, A, B, alpha, dA=dA2, dB=dB2, accumulate=True)
+    assert torch.equal(dA2, 2 * dA1) and torch.equal(dB2, 2 * dB1)
+    # a stale value in the outputs is overwritten without accumulate
+    dA2.fill_(float("nan"))
+    dB2.fill_(float("nan"))
+    qops.lora_grad(x, dy, A, B, alpha, dA=dA2, dB=dB2)
+    assert torch.equal(dA1, dA2) and torch.equal(dB1, dB2)
+
+
+def test_adapter_grad_rank_one_closed_form(qops):
+    """One non-zero in each adapter and one-hot rows of x and dY: every output
+    is a single product, so the gradients are exact."""
+    M, N, K, r, alpha = 70, 72, 128, 4, 8.0
+    A = np.zeros((r, K), np.float32)
+    B = np.zeros((N, r), np.float32)
+    A[1, 100] = 0.75
+    B[9, 1] = -0.5
+    x = np.zeros((M, K), np.float32)
+    dy = np.zeros((M, N), np.float32)
+    x[66, 100] = 1.0
+    dy[66, 9] = 1.0
+    bits = synth.to_bf16_bits
+    dA, dB = qops.lora_grad(dev(bits(x)), dev(bits(dy)), dev(bits(A)), dev(bits(B)), alpha)
+    eA = np.zeros((r, K), np.float32)
+    eB = np.zeros((N, r), np.float32)
+    eA[1, 100] = 2.0 * -0.5          # s * u[66, 1] * x[66, 100], u = dY . B
+    eB[9, 1] = 2.0 * 0.75            # s * dY[66, 9] * t[66, 1], t = x . A^T
+    assert np.array_equal(dA.cpu().numpy(), eA) and np.array_equal(dB.cpu().numpy(), eB)
+
+
+@pytest.mark.parametrize("name", ["7b_mlp_up", "65b_up"])
+def test_adapter_grad_full_size(qops, name):
+    """Every gradient entry at full size: against the fp64 oracle (exact t, u)
+    within the stated tolerance, and against an fp32 torch reference that
+    rounds t and u to bf16 as the kernels do, to 1e-4."""
+    inp = synth.config_inputs(name, None)
+    M, N, K, r, alpha = inp["M"], inp["N"], inp["K"], inp["r"], inp["alpha"]
+    x, dy, A, B = dev(inp["x"]), dev(inp["dy"]), dev(inp["A"]), dev(inp["B"])
+    dA, dB = qops.lora_grad(x, dy, A, B, alpha)
+    s = alpha / r
+    t = (x.float() @ A.float().t()).bfloat16().float()
+    u = (dy.float() @ B.float()).bfloat16().float()
+    rA = s * (u.t() @ x.float())
+    rB = s * (dy.float().t() @ t)
+    assert (torch.linalg.norm(dA - rA) / torch.linalg.norm(rA)).item() <= 1e-4
+    assert (torch.linalg.norm(dB - rB) / torch.linalg.norm(rB)).item() <= 1e-4
+    gA, gB = dA.cpu().numpy().astype(np.float64), dB.cpu().numpy().astype(np.float64)
+    del x, dy, A, B, dA, dB, t, u, rA, rB
+    torch.cuda.empty_cache()
+    oA, oB = gemm.lora_grads(inp["x"], inp["dy"], inp["A"], inp["B"], alpha, r)
+    assert rel_fro(gA, oA) <= TIGHT and rel_fro(gB, oB) <= TIGHT
