@@ -146,7 +146,8 @@ size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r);
  *           qlora_workspace_bytes(0, M, N, K, r) bytes, 16-byte aligned
  *           (may be NULL when that is 0). Its contents are overwritten.
  * Products are bf16 x bf16 accumulated in fp32. x, packed, y, A, B and the
- * workspace must be 16-byte aligned.
+ * workspace must be 16-byte aligned. Size limits (here and in the two calls
+ * below): M <= 2^31, N and K <= 2^24.
  */
 int qlora_nf4_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K,
                        const uint8_t* packed, const int8_t* qscale,

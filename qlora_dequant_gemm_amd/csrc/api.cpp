@@ -128,7 +128,7 @@ int qlora_nf4_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K, const
   int st = check_weight(packed, qscale, step);
   if (st) return st;
   if (M < 1 || N < 1 || K < 64 || K % QLORA_BLOCK != 0) return QLORA_ERR_SHAPE;
-  if (M > (int64_t{1} << 31) || N > (int64_t{1} << 31) || K > (int64_t{1} << 31)) return QLORA_ERR_SHAPE;
+  if (M > (int64_t{1} << 31) || N > (int64_t{1} << 24) || K > (int64_t{1} << 24)) return QLORA_ERR_SHAPE;
   st = check_adapter(A, B, r);
   if (st) return st;
   if (!aligned16(x) || !aligned16(y)) return QLORA_ERR_ALIGN;
@@ -147,7 +147,7 @@ int qlora_nf4_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K, const 
   int st = check_weight(packed, qscale, step);
   if (st) return st;
   if (M < 1 || N < 1 || N % 8 != 0 || K < 64 || K % QLORA_BLOCK != 0) return QLORA_ERR_SHAPE;
-  if (M > (int64_t{1} << 31) || N > (int64_t{1} << 31) || K > (int64_t{1} << 31)) return QLORA_ERR_SHAPE;
+  if (M > (int64_t{1} << 31) || N > (int64_t{1} << 24) || K > (int64_t{1} << 24)) return QLORA_ERR_SHAPE;
   st = check_adapter(A, B, r);
   if (st) return st;
   if (!aligned16(dy) || !aligned16(dx)) return QLORA_ERR_ALIGN;
@@ -164,7 +164,7 @@ int qlora_lora_grad(const uint16_t* x, const uint16_t* dy, int64_t M, int64_t N,
                     size_t ws_bytes, void* stream) {
   if (!x || !dy || !dA || !dB) return QLORA_ERR_NULL;
   if (M < 1 || N < 1 || N % 8 != 0 || K < 64 || K % QLORA_BLOCK != 0) return QLORA_ERR_SHAPE;
-  if (M > (int64_t{1} << 31) || N > (int64_t{1} << 31) || K > (int64_t{1} << 31)) return QLORA_ERR_SHAPE;
+  if (M > (int64_t{1} << 31) || N > (int64_t{1} << 24) || K > (int64_t{1} << 24)) return QLORA_ERR_SHAPE;
   if (r < 1 || r > QLORA_MAX_RANK) return QLORA_ERR_RANK;
   if (!A || !B) return QLORA_ERR_NULL;
   if (accumulate != 0 && accumulate != 1) return QLORA_ERR_SHAPE;

@@ -719,7 +719,8 @@ hipError_t launch_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K, c
   const int rp = r > 0 ? static_cast<int>(rank_pad(r)) : 0;
   void* lora = r > 0 ? static_cast<void*>(wsb + L.lora_off) : nullptr;
   if (r > 0) {
-    const hipError_t e = launch_lora_down(true, x, M, K, A, r, lora, stream, nullptr);
+    const hipError_t e = launch_lora_down(true, x, M, K, A, r, lora, stream, nullptr,
+                                          reinterpret_cast<float*>(wsb + L.dp_off));
     if (e != hipSuccess) return e;
   }
   if (M <= kSmallM)
@@ -750,7 +751,8 @@ hipError_t launch_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K, co
                             reinterpret_cast<float*>(wsb + L.part_off), dx, cb, stream);
   if (r > 0) {
     const hipError_t e = launch_lora_down(false, dy, M, N, B, r, lora, stream,
-                                          reinterpret_cast<uint16_t*>(wsb + L.bt_off));
+                                          reinterpret_cast<uint16_t*>(wsb + L.bt_off),
+                                          reinterpret_cast<float*>(wsb + L.dp_off));
     if (e != hipSuccess) return e;
   }
   const int64_t tiles = cdiv(M, kTile) * cdiv(K, kTile);

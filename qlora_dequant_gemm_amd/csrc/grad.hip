@@ -236,12 +236,12 @@ GradPlan grad_plan(int64_t M, int64_t N, int64_t K, int r) {
   // rows of t^T / u^T: the rank tiles the gradient kernel reads (16 NT, NT the
   // power of two >= ceil(r / 16)) may exceed rp; rows past rp are never
   // written and feed only output ranks >= r, which are not stored
-  const int64_t nt = (r + 15) / 16;
-  const int64_t rows = std::max<int64_t>(g.rp, 16 * (nt <= 1 ? 1 : nt == 2 ? 2 : nt <= 4 ? 4 : 8));
+  const int64_t rows = std::max<int64_t>(g.rp, 16 * down_nt(r));
   g.tt_off = take(static_cast<size_t>(rows) * g.Mp * 2);
   g.ut_off = take(static_cast<size_t>(rows) * g.Mp * 2);
   g.pb_off = take(static_cast<size_t>(g.SB) * N * r * 4);
   g.pa_off = take(static_cast<size_t>(g.SA) * K * r * 4);
+  g.dp_off = take(std::max(down_plan(M, K, r).part_bytes, down_plan(M, N, r).part_bytes));
   g.total = off;
   return g;
 }
@@ -256,13 +256,14 @@ hipError_t launch_lora_grad(const uint16_t* x, const uint16_t* dy, int64_t M, in
   uint16_t* ut = reinterpret_cast<uint16_t*>(wsb + g.ut_off);
   float* pb = reinterpret_cast<float*>(wsb + g.pb_off);
   float* pa = reinterpret_cast<float*>(wsb + g.pa_off);
-  hipError_t e = launch_lora_down(true, x, M, K, A, r, tt, stream, nullptr, g.Mp);     // t^T [rp][Mp]
+  float* dp = reinterpret_cast<float*>(wsb + g.dp_off);
+  hipError_t e = launch_lora_down(true, x, M, K, A, r, tt, stream, nullptr, dp, g.Mp);     // t^T [rp][Mp]
   if (e != hipSuccess) return e;
-  e = launch_lora_down(false, dy, M, N, B, r, ut, stream, bt, g.Mp);                  // u^T [rp][Mp]
+  e = launch_lora_down(false, dy, M, N, B, r, ut, stream, bt, dp, g.Mp);                  // u^T [rp][Mp]
   if (e != hipSuccess) return e;
   const int ctb = static_cast<int>(cdiv(N, kGradCols)), cta = static_cast<int>(cdiv(K, kGradCols));
   const int SB = static_cast<int>(g.SB), SA = static_cast<int>(g.SA);
-  const int nt = (r + 15) / 16;
+  const int nt = down_nt(r);
 #define QNF4_GRAD(NTV)                                                                                         \
   do {                                                                                                         \
     hipLaunchKernelGGL(HIP_KERNEL_NAME(k_lora_grad<NTV, false>), dim3(ctb * SB), dim3(256), 0, stream, dy, M, N, \

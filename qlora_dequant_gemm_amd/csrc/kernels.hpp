@@ -40,10 +40,40 @@ inline int64_t bwd_small_splits(int64_t N, int64_t K) {
   return s;
 }
 
+// Tiled down-projection (M > kSmallM, and the adapter gradients): 64-row tiles
+// x KS splits of the contraction, `sps` 32-deep steps each; with KS > 1 the
+// splits write fp32 partials [KS][Mr][16 nt] (Mr = M rounded up to 64) that a
+// second kernel sums in order. nt = rank tiles of 16 the kernel computes (a
+// power of two >= ceil(r / 16)).
+struct DownPlan {
+  int64_t KS = 1, sps = 0, Mr = 0;
+  int nt = 1;
+  size_t part_bytes = 0;
+};
+inline int down_nt(int r) {
+  const int n = (r + 15) / 16;
+  return n <= 1 ? 1 : n == 2 ? 2 : n <= 4 ? 4 : 8;
+}
+inline DownPlan down_plan(int64_t M, int64_t Kc, int r) {
+  DownPlan p;
+  p.nt = down_nt(r);
+  const int64_t tiles = cdiv(M, 64), nsteps = cdiv(Kc, 32);
+  int64_t ks = cdiv(256, tiles);               // about one workgroup per CU
+  const int64_t kmax = cdiv(nsteps, 8);        // at least 8 steps per split
+  if (ks > kmax) ks = kmax;
+  if (ks < 1) ks = 1;
+  p.sps = cdiv(nsteps, ks);
+  p.KS = cdiv(nsteps, p.sps);
+  p.Mr = tiles * 64;
+  if (p.KS > 1) p.part_bytes = align256(static_cast<size_t>(p.KS * p.Mr * 16 * p.nt * 4));
+  return p;
+}
+
 struct WsLayout {
   size_t lora_off = 0, lora_bytes = 0;    // t or u (bf16 [M][rp], or fp32 partials)
   size_t part_off = 0, part_bytes = 0;    // small-M backward partials
   size_t bt_off = 0, bt_bytes = 0;        // large-M backward: B transposed, bf16 [r][N]
+  size_t dp_off = 0, dp_bytes = 0;        // large M: split partials of the down-projection
   size_t total = 0;
 };
 
@@ -65,7 +95,9 @@ inline WsLayout ws_layout(int op, int64_t M, int64_t N, int64_t K, int r) {
     w.part_bytes = align256(static_cast<size_t>(bwd_small_splits(N, K) * M * K * 4));
   w.bt_off = w.part_off + w.part_bytes;
   if (op == 1 && M > kSmallM && r > 0) w.bt_bytes = align256(static_cast<size_t>(r) * N * 2);
-  w.total = w.lora_bytes + w.part_bytes + w.bt_bytes;
+  w.dp_off = w.bt_off + w.bt_bytes;
+  if (M > kSmallM && r > 0) w.dp_bytes = down_plan(M, op == 0 ? K : N, r).part_bytes;
+  w.total = w.lora_bytes + w.part_bytes + w.bt_bytes + w.dp_bytes;
   return w;
 }
 
@@ -73,7 +105,7 @@ inline WsLayout ws_layout(int op, int64_t M, int64_t N, int64_t K, int r) {
 // the transposed t and u); SB / SA = row splits of the dY and x contractions.
 struct GradPlan {
   int64_t Mp = 0, rp = 0, SB = 1, SA = 1;
-  size_t bt_off = 0, tt_off = 0, ut_off = 0, pb_off = 0, pa_off = 0, total = 0;
+  size_t bt_off = 0, tt_off = 0, ut_off = 0, pb_off = 0, pa_off = 0, dp_off = 0, total = 0;
 };
 GradPlan grad_plan(int64_t M, int64_t N, int64_t K, int r);
 
@@ -87,12 +119,13 @@ hipError_t launch_dequant(const uint8_t* packed, const int8_t* qscale, const flo
                           uint16_t* out, const Codebook& cb, hipStream_t stream);
 
 // rank-r down projection of `in` [M][Kc] by the adapter (wrow: A [r][Kc];
-// else B [Kc][r]); M <= kSmallM writes lora_splits fp32 partials, else bf16
-// [M][rp]. ldt > 0: bf16 transposed, out [rp][ldt] (ldt a multiple of 16, >= M,
-// rows past M zero), for any M.
-// wt: workspace for the transposed adapter (bf16 path, wrow == false; r * Kc bf16)
+// else B [Kc][r]); M <= kSmallM (ldt == 0) writes lora_splits fp32 partials,
+// else bf16 [M][rp]; ldt > 0: bf16 transposed, out [rp][ldt] (ldt = M rounded
+// up to 64, rows past M zero), for any M.
+// wt: workspace for the transposed adapter (bf16 path, wrow == false; r * Kc
+// bf16); part: down_plan(M, Kc, r).part_bytes of workspace (bf16 path).
 hipError_t launch_lora_down(bool wrow, const uint16_t* in, int64_t M, int64_t Kc, const uint16_t* W, int r,
-                            void* out, hipStream_t stream, uint16_t* wt, int64_t ldt = 0);
+                            void* out, hipStream_t stream, uint16_t* wt, float* part, int64_t ldt = 0);
 hipError_t launch_fwd_small(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
                             const int8_t* qscale, const float* step, const float* tpart, int St, int rp,
                             const uint16_t* B, int r, float scale, uint16_t* y, const Codebook& cb,

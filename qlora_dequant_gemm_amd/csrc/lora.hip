@@ -30,63 +30,103 @@ __device__ __forceinline__ u32x4 adapter8(const uint16_t* __restrict__ W, int64_
 }
 
 // ---------------------------------------------------------------------------
-// Large M: out bf16 [M][rp]. Grid ceil(M/16): the 4 waves of a workgroup share
-// 16 rows and take the 32-deep contraction steps round robin (operands straight
-// from global memory; the adapter stays in L2), then reduce through LDS.
+// Large M (and the transposed outputs of the adapter gradients): 64-row tiles
+// x KS splits of the contraction. Wave w owns rows 16w .. 16w + 15 of the
+// tile and every rank tile, so each adapter fragment is used by 64 rows of
+// the workgroup (once per wave, from L1/L2); all loads of a group of GS steps
+// are issued before its MFMAs. Operands come through buffer descriptors: rows
+// past M read as zero, and so do adapter rows past r; a step's lanes past Kc
+// (Kc % 32 != 0) get a zeroed adapter fragment. KS == 1 writes bf16 directly
+// (padding ranks up to rp zero), else fp32 partials [KS][Mr][16 NT] that
+// k_down_finish sums in order.
 // ---------------------------------------------------------------------------
-// NT: 16-wide rank tiles holding real ranks (ceil(r / 16)); the padding
-// columns up to rp are written as zero. TRANS writes the result transposed,
-// out [rp][ldt] with ldt >= M, rows m in [M, ldt) zero (the grid then covers
-// ldt / 16 row tiles). Each wave takes 32-deep contraction
-// steps round robin in groups of 8, all of a group's loads issued before its
-// MFMAs, so that enough loads are in flight to stream `in` from HBM.
-template <int NT, bool TRANS>
-__global__ __launch_bounds__(256) void k_lora_down(const uint16_t* __restrict__ in, int64_t M, int64_t Kc,
-                                                   const uint16_t* __restrict__ W, int r, int rp,
-                                                   uint16_t* __restrict__ out, int64_t ldt) {
-  __shared__ f32x4 red[4][8][64];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+constexpr int kBufWord3 = 0x00020000;          // raw buffer descriptor word 3 on gfx9-family parts
+
+template <int NT, int GS>
+__global__ __launch_bounds__(256) void k_down(const uint16_t* in, int64_t M, int64_t Kc, const uint16_t* W, int r,
+                                              int rp, int64_t sps, int KS, float* __restrict__ part,
+                                              uint16_t* __restrict__ out, int64_t ldt) {
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int g = lane >> 4, c = lane & 15;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * 16;
-  const int ntile = rp / 16;
-  const uint16_t* in_row = in + imin(m0 + c, M - 1) * Kc;
+  const int tile = blockIdx.x / KS, ks = blockIdx.x % KS;
+  const int64_t m0 = static_cast<int64_t>(tile) * 64;
   const int64_t nsteps = cdiv(Kc, 32);
-  f32x4 acc[8];
+  const int64_t st0 = ks * sps, st1 = imin(nsteps, st0 + sps);
+  const int64_t rows_valid = imin(64, M - m0);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(in + m0 * Kc), 0, static_cast<int>(rows_valid * Kc * 2), kBufWord3);
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(W), 0, static_cast<int>(static_cast<int64_t>(r) * Kc * 2), kBufWord3);
+  const uint32_t xoff = static_cast<uint32_t>(((16 * w + c) * Kc + 8 * g) * 2);
+  uint32_t woff[NT];
 #pragma unroll
-  for (int jt = 0; jt < 8; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  constexpr int kGroup = 8;
-  for (int64_t st0 = w * kGroup; st0 < nsteps; st0 += 4 * kGroup) {
-    u32x4 xa[kGroup], wa[kGroup][NT];
+  for (int jt = 0; jt < NT; ++jt) woff[jt] = static_cast<uint32_t>(((16 * jt + c) * Kc + 8 * g) * 2);
+  f32x4 acc[NT];
 #pragma unroll
-    for (int u = 0; u < kGroup; ++u) {
-      const int64_t k = (st0 + u) * 32 + 8 * g;
-      const bool kin = st0 + u < nsteps && k < Kc;
-      xa[u] = kin ? ld16(in_row + k) : u32x4{0u, 0u, 0u, 0u};
+  for (int jt = 0; jt < NT; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int64_t st = st0; st < st1; st += GS) {
+    u32x4 xa[GS], wa[GS][NT];
 #pragma unroll
-      for (int jt = 0; jt < NT; ++jt) wa[u][jt] = kin ? adapter8<true>(W, Kc, r, 16 * jt + c, k) : u32x4{0u, 0u, 0u, 0u};
+    for (int u = 0; u < GS; ++u) {
+      const uint32_t so = static_cast<uint32_t>(imin(st + u, st1 - 1) * 64);
+      xa[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff, so, 0));
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt)
+        wa[u][jt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, woff[jt], so, 0));
     }
 #pragma unroll
-    for (int u = 0; u < kGroup; ++u)
+    for (int u = 0; u < GS; ++u) {
+      // a clamped repeat of the last step, or lanes past Kc: no contribution
+      const bool live = st + u < st1 && (st + u) * 32 + 8 * g < Kc;
 #pragma unroll
-      for (int jt = 0; jt < NT; ++jt) acc[jt] = mfma16(as_bf16x8(xa[u]), as_bf16x8(wa[u][jt]), acc[jt]);
-  }
-#pragma unroll
-  for (int jt = 0; jt < 8; ++jt)
-    if (jt < ntile) red[w][jt][lane] = acc[jt];
-  __syncthreads();
-  for (int idx = t; idx < ntile * 64; idx += 256) {
-    const int jt = idx >> 6, ln = idx & 63;
-    const f32x4 sum = red[0][jt][ln] + red[1][jt][ln] + red[2][jt][ln] + red[3][jt][ln];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t m = m0 + 4 * (ln >> 4) + v;
-      if (TRANS) {
-        if (m < ldt) out[(16 * jt + (ln & 15)) * ldt + m] = m < M ? bf16_bits(sum[v]) : uint16_t{0};
-      } else if (m < M) {
-        out[m * rp + 16 * jt + (ln & 15)] = bf16_bits(sum[v]);
+      for (int jt = 0; jt < NT; ++jt) {
+        const u32x4 b = live ? wa[u][jt] : u32x4{0u, 0u, 0u, 0u};
+        acc[jt] = mfma16(as_bf16x8(xa[u]), as_bf16x8(b), acc[jt]);
       }
     }
   }
+  // lane holds rows 16w + 4g + v of the tile, rank 16 jt + c
+  if (KS > 1) {
+    float* dst = part + (static_cast<int64_t>(ks) * (cdiv(M, 64) * 64) + m0 + 16 * w + 4 * g) * (16 * NT);
+#pragma unroll
+    for (int jt = 0; jt < NT; ++jt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) dst[v * 16 * NT + 16 * jt + c] = acc[jt][v];
+    return;
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int64_t m = m0 + 16 * w + 4 * g + v;
+    if (ldt) {
+      if (m >= ldt) continue;
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt)
+        if (16 * jt + c < rp) out[(16 * jt + c) * ldt + m] = m < M ? bf16_bits(acc[jt][v]) : uint16_t{0};
+      for (int j = 16 * NT + c; j < rp; j += 16) out[j * ldt + m] = 0;
+    } else if (m < M) {
+#pragma unroll
+      for (int jt = 0; jt < NT; ++jt)
+        if (16 * jt + c < rp) out[m * rp + 16 * jt + c] = bf16_bits(acc[jt][v]);
+      for (int j = 16 * NT + c; j < rp; j += 16) out[m * rp + j] = 0;
+    }
+  }
+}
+
+// Sum of the KS split partials in order, rounded to bf16, written [M][rp] or
+// transposed [rp][ldt] (rows past M and ranks past 16 nt zero).
+__global__ __launch_bounds__(256) void k_down_finish(const float* __restrict__ part, int KS, int64_t M,
+                                                     int64_t Mr, int cols, int rp, uint16_t* __restrict__ out,
+                                                     int64_t ldt) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t rows = ldt ? ldt : M;
+  if (idx >= rows * rp) return;
+  const int64_t m = ldt ? idx % ldt : idx / rp;
+  const int j = static_cast<int>(ldt ? idx / ldt : idx % rp);
+  float sum = 0.f;
+  if (m < M && j < cols)
+    for (int ks = 0; ks < KS; ++ks) sum += part[(ks * Mr + m) * cols + j];
+  out[ldt ? j * ldt + m : m * rp + j] = bf16_bits(sum);
 }
 
 // ---------------------------------------------------------------------------
@@ -134,17 +174,27 @@ __global__ __launch_bounds__(512) void k_lora_down_small(const uint16_t* __restr
   }
 }
 
-// B [N][r] -> Bt [r][N] (the large-M backward contracts over N, so it reads
-// the adapter row-major through this copy)
+// B [N][r] -> Bt [r][N] (the backward contracts over N, so it reads the
+// adapter row-major through this copy): 64 rows of B (one contiguous run of
+// 128 r bytes) staged in LDS, then each rank's 64 values written contiguously.
 __global__ __launch_bounds__(256) void k_adapter_t(const uint16_t* __restrict__ B, int64_t N, int r,
                                                    uint16_t* __restrict__ Bt) {
-  const int64_t n = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (n >= N) return;
-  for (int j = 0; j < r; ++j) Bt[static_cast<int64_t>(j) * N + n] = B[n * r + j];
+  __shared__ uint16_t tileb[64 * 128];
+  const int t = threadIdx.x;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int nrows = static_cast<int>(imin(64, N - n0));
+  const int n16 = nrows * r / 8;                 // 16-byte pieces (N % 8 == 0: r * nrows % 8 == 0)
+  const u32x4* src = reinterpret_cast<const u32x4*>(B + n0 * r);
+  for (int i = t; i < n16; i += 256) reinterpret_cast<u32x4*>(tileb)[i] = src[i];
+  __syncthreads();
+  for (int i = t; i < r * 64; i += 256) {
+    const int j = i >> 6, nn = i & 63;
+    if (nn < nrows) Bt[j * N + n0 + nn] = tileb[nn * r + j];
+  }
 }
 
 hipError_t launch_lora_down(bool wrow, const uint16_t* in, int64_t M, int64_t Kc, const uint16_t* W, int r,
-                            void* out, hipStream_t stream, uint16_t* wt, int64_t ldt) {
+                            void* out, hipStream_t stream, uint16_t* wt, float* part, int64_t ldt) {
   const int rp = static_cast<int>(rank_pad(r));
   if (M <= kSmallM && ldt == 0) {
     const int S = static_cast<int>(lora_splits(M, Kc));
@@ -154,31 +204,33 @@ hipError_t launch_lora_down(bool wrow, const uint16_t* in, int64_t M, int64_t Kc
     else
       hipLaunchKernelGGL(k_lora_down_small<false>, dim3(S), dim3(512), 0, stream, in, M, Kc, W, r, rp, S,
                          static_cast<float*>(out));
-  } else {
-    const unsigned grid = static_cast<unsigned>(cdiv(ldt ? ldt : M, 16));
-    const uint16_t* Wr = W;
-    if (!wrow) {
-      hipLaunchKernelGGL(k_adapter_t, dim3(static_cast<unsigned>(cdiv(Kc, 256))), dim3(256), 0, stream, W, Kc, r,
-                         wt);
-      Wr = wt;
-    }
-    const int nt = (r + 15) / 16;
-#define QNF4_LDOWN(NTV)                                                                                     \
-  if (ldt)                                                                                                  \
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(k_lora_down<NTV, true>), dim3(grid), dim3(256), 0, stream, in, M, Kc, \
-                       Wr, r, rp, static_cast<uint16_t*>(out), ldt);                                        \
-  else                                                                                                      \
-    hipLaunchKernelGGL(HIP_KERNEL_NAME(k_lora_down<NTV, false>), dim3(grid), dim3(256), 0, stream, in, M, Kc, \
-                       Wr, r, rp, static_cast<uint16_t*>(out), ldt)
-    if (nt <= 1)
-      QNF4_LDOWN(1);
-    else if (nt == 2)
-      QNF4_LDOWN(2);
-    else if (nt <= 4)
-      QNF4_LDOWN(4);
-    else
-      QNF4_LDOWN(8);
-#undef QNF4_LDOWN
+    return hipGetLastError();
+  }
+  const uint16_t* Wr = W;
+  if (!wrow) {
+    hipLaunchKernelGGL(k_adapter_t, dim3(static_cast<unsigned>(cdiv(Kc, 64))), dim3(256), 0, stream, W, Kc, r, wt);
+    Wr = wt;
+  }
+  const DownPlan p = down_plan(M, Kc, r);
+  const unsigned grid = static_cast<unsigned>(cdiv(M, 64) * p.KS);
+  const int KS = static_cast<int>(p.KS);
+  uint16_t* o = static_cast<uint16_t*>(out);
+#define QNF4_DOWN(NTV, GSV)                                                                                      \
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(k_down<NTV, GSV>), dim3(grid), dim3(256), 0, stream, in, M, Kc, Wr, r, rp, \
+                     p.sps, KS, part, o, ldt)
+  if (p.nt == 1)
+    QNF4_DOWN(1, 8);
+  else if (p.nt == 2)
+    QNF4_DOWN(2, 8);
+  else if (p.nt == 4)
+    QNF4_DOWN(4, 4);
+  else
+    QNF4_DOWN(8, 2);
+#undef QNF4_DOWN
+  if (KS > 1) {
+    const int64_t n = (ldt ? ldt : M) * rp;
+    hipLaunchKernelGGL(k_down_finish, dim3(static_cast<unsigned>(cdiv(n, 256))), dim3(256), 0, stream, part, KS, M,
+                       p.Mr, 16 * p.nt, rp, o, ldt);
   }
   return hipGetLastError();
 }

@@ -53,7 +53,8 @@ def test_codebook_bitwise_equals_oracle():
 def test_workspace_sizes():
     ws = ops.workspace_bytes
     assert ws(0, 4096, 11008, 4096, 0) == 0
-    assert ws(0, 4096, 11008, 4096, 16) == 4096 * 32 * 2          # bf16 t, rank padded to 32
+    # bf16 t (rank padded to 32) + fp32 partials of 4 contraction splits (16 ranks)
+    assert ws(0, 4096, 11008, 4096, 16) == 4096 * 32 * 2 + 4 * 4096 * 16 * 4
     assert ws(0, 16, 4096, 4096, 16) == 16 * 16 * 32 * 4          # 16 K-slices of fp32 partials
     assert ws(1, 16, 4096, 4096, 0) > 0                           # small-M backward partials
     assert ws(1, 4096, 4096, 11008, 0) == 0
