@@ -159,6 +159,22 @@ class Workload:
         labels = [lab for lab, _ in self.calls(0)]
         return [(lab, [self.calls(c)[i][1] for c in range(self.C)]) for i, lab in enumerate(labels)]
 
+    def extra_groups(self):
+        """Calls timed beside the step but not part of it: the adapter gradients
+        (training shapes only)."""
+        if self.decode:
+            return []
+        M = max(self.Ms)
+        N, K, r = self.N, self.K, self.r
+        dev = "cuda"
+        self.dA = self.torch.empty((r, K), dtype=self.torch.float32, device=dev)
+        self.dB = self.torch.empty((N, r), dtype=self.torch.float32, device=dev)
+        self.ws.get(self.ops.workspace_bytes(2, M, N, K, r))
+        fn = lambda: self.ops.lora_grad(self.x[M], self.dy[M], self.A, self.B, self.alpha, dA=self.dA, dB=self.dB,
+                                        ws=self.ws)
+        work = (2 * M * (K + N) + 4 * r * (K + N), 2 * M * r * (K + N))
+        return [(f"lora_grad_M{M}", [fn] * 4, work)]
+
     def describe(self):
         shapes = {"7b_attn": "7B attention projection W 4096x4096", "7b_mlp_up": "7B MLP up W 11008x4096",
                   "7b_mlp_down": "7B MLP down W 4096x11008", "65b_up": "65B up W 22016x8192",
@@ -246,6 +262,9 @@ class StackWorkload:
                 f"{self.L * len(self.lin)} linears; step = {self.L * len(self.lin)} fused fwd at M={self.M} "
                 f"in layer order, then {self.L * len(self.lin)} fused bwd dX in reverse")
 
+    def extra_groups(self):
+        return []
+
     def config_extra(self):
         return {"layers": self.L, "linears": [list(t) for t in self.lin], "nf4_resident_bytes": self.nf4_bytes}
 
@@ -293,7 +312,9 @@ def run_gpu(args):
     # linear in every layer); events on the launch stream bracket `reps`
     # replays of that graph
     per_call = {}
-    for lab, fns in wl.timing_groups():
+    extra = {}
+    groups = [(lab, fns, None) for lab, fns in wl.timing_groups()] + wl.extra_groups()
+    for lab, fns, work in groups:
         reps = max(2, args.steps // len(fns))
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
@@ -309,7 +330,14 @@ def run_gpu(args):
                 g.replay()
             e1.record(stream)
         torch.cuda.synchronize()
-        per_call[lab] = e0.elapsed_time(e1) / (reps * len(fns))
+        ms = e0.elapsed_time(e1) / (reps * len(fns))
+        if work is None:
+            per_call[lab] = ms
+        else:
+            extra[lab] = {"ms": round(ms, 5), "GB/s": round(work[0] / ms / 1e6, 1),
+                          "hbm_frac": round(work[0] / ms / 1e6 / HBM_PEAK_GBS, 4),
+                          "TFLOP/s": round(work[1] / ms / 1e9, 2)}
+    wl.extra = extra
     return wl, ms_step, per_call, wall
 
 
@@ -530,6 +558,10 @@ def main():
         "kernels": kernels,
         "step_bytes": step_bytes, "step_flops": step_flops,
     }
+    if wl.extra:
+        line["outside_step"] = dict(wl.extra, note="adapter gradients dA, dB (qlora_lora_grad) at the step's "
+                                                   "shapes, timed alone; GB/s counts x and dY read once and "
+                                                   "dA, dB written")
     if not args.no_cpu_baseline:
         if isinstance(wl, StackWorkload):
             line["cpu_baseline"] = cpu_baseline_stack(args, wl)
