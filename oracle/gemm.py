@@ -15,6 +15,12 @@ Sources, cited by page title and section:
   [STEP]      "QLoRA" (techbytebybyte), section "Follow one QLoRA training
               step": gradients go into the adapters, not the frozen base.
 
+  [MERGE]     "QLoRA" (techbytebybyte), "Curiosity question: is the final
+              model permanently 4-bit?", "Training setup versus deployment
+              setup" and "Common misconception" (the adapter can be merged
+              back into the weights for deployment); "A 65B fine-tune on the
+              GPU you already have", figure 2 (same low-rank update, same
+              mergeability).
   [BASE]      "QLoRA Explained: ...", "What is QLoRA?" (the base is frozen:
               gradients and optimizer state exist only for the adapters);
               "QLoRA and Quantized Training", "The idea" (the adapters hold
@@ -25,6 +31,7 @@ Definitions (the LoRA scale alpha/r is the standard one for these knobs):
   backward  dX = dY . W'  [+ (alpha/r) . (dY . B) . A]
   adapters  dB = (alpha/r) . dY^T . (x . A^T)      [N, r]
             dA = (alpha/r) . (dY . B)^T . x        [r, K]
+  merge     W'' = W' + (alpha/r) . B . A             [N, K]
 with W' [N,K] the dequantized bf16 weight, x [M,K], A [r,K], B [N,r],
 dY [M,N]. The adapter gradients are those of the scalar <dY, y> with respect
 to B and A: y is linear in each adapter with the other held fixed. Inputs are bf16 bit patterns (uint16); the products are taken in
@@ -115,3 +122,13 @@ def lora_grads(x_bits, dy_bits, A_bits, B_bits, alpha, r):
     t = x @ A.T
     u = dy @ B
     return s * (u.T @ x), s * (dy.T @ t)
+
+
+def merge(wdeq_bits, A_bits=None, B_bits=None, alpha=0.0, r=0):
+    """W' + (alpha/r) . B . A [N,K] in fp64 ([MERGE], [ARCH-fig2]): the one
+    dense weight whose forward equals the adapted layer's, x . W''^T =
+    x . W'^T + (alpha/r) . (x . A^T) . B^T."""
+    W = bf16_to_f64(wdeq_bits)
+    if not r:
+        return W
+    return W + (alpha / r) * (bf16_to_f64(B_bits) @ bf16_to_f64(A_bits))

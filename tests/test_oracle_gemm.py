@@ -185,3 +185,32 @@ def test_adapter_grads_one_hot_closed_form():
     eB[5] = 2.0 * gemm.bf16_to_f64(A)[:, 37]
     eA[:, 37] = 2.0 * gemm.bf16_to_f64(B)[5]
     assert np.array_equal(dA, eA) and np.array_equal(dB, eB)
+
+
+# ---------------------------------------------------------------------------
+# merge of the adapter into one dense weight
+# ---------------------------------------------------------------------------
+def test_merge_forward_equals_adapted_forward():
+    """x . W''^T == x . W'^T + s . (x . A^T) . B^T (associativity), on a
+    non-square shape so that a transposed or swapped product cannot pass."""
+    M, N, K, r = 7, 40, 192, 5
+    wd, x, A, B, _ = _setup(M, N, K, r, 330)
+    merged = gemm.merge(wd, A, B, 6.0, r)
+    assert merged.shape == (N, K)
+    lhs = gemm.bf16_to_f64(x) @ merged.T
+    rhs = gemm.lora_forward(x, wd, A, B, 6.0, r)
+    assert np.allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
+
+
+def test_merge_without_adapter_and_rank_one():
+    N, K, r = 16, 64, 4
+    wd, _, _, _, _ = _setup(1, N, K, 0, 340)
+    assert np.array_equal(gemm.merge(wd), gemm.bf16_to_f64(wd))
+    A = np.zeros((r, K), np.float32)
+    B = np.zeros((N, r), np.float32)
+    A[3, 10] = 0.25
+    B[7, 3] = 2.0
+    m = gemm.merge(np.zeros((N, K), np.uint16), _bits(A), _bits(B), 8.0, r)
+    e = np.zeros((N, K))
+    e[7, 10] = 2.0 * 0.25 * 2.0
+    assert np.array_equal(m, e)
