@@ -173,7 +173,11 @@ class Workload:
         fn = lambda: self.ops.lora_grad(self.x[M], self.dy[M], self.A, self.B, self.alpha, dA=self.dA, dB=self.dB,
                                         ws=self.ws)
         work = (2 * M * (K + N) + 4 * r * (K + N), 2 * M * r * (K + N))
-        return [(f"lora_grad_M{M}", [fn] * 4, work)]
+        self.merged = self.torch.empty((N, K), dtype=self.torch.bfloat16, device=dev)
+        qw = self.qw[self.C // 2]
+        mfn = lambda: self.ops.merge(qw, self.A, self.B, self.alpha, out=self.merged)
+        mwork = (N * K * (NF4_BYTES_PER_PARAM + 2) + 2 * r * (K + N), 2 * N * K * r)
+        return [(f"lora_grad_M{M}", [fn] * 4, work), ("merge", [mfn] * 4, mwork)]
 
     def describe(self):
         shapes = {"7b_attn": "7B attention projection W 4096x4096", "7b_mlp_up": "7B MLP up W 11008x4096",
@@ -559,9 +563,10 @@ def main():
         "step_bytes": step_bytes, "step_flops": step_flops,
     }
     if wl.extra:
-        line["outside_step"] = dict(wl.extra, note="adapter gradients dA, dB (qlora_lora_grad) at the step's "
-                                                   "shapes, timed alone; GB/s counts x and dY read once and "
-                                                   "dA, dB written")
+        line["outside_step"] = dict(wl.extra, note="timed alone at the step's shapes: adapter gradients dA, "
+                                                   "dB (qlora_lora_grad; GB/s counts x and dY read once and "
+                                                   "dA, dB written) and the adapter merged into one bf16 "
+                                                   "weight (qlora_nf4_merge; NF4 read + bf16 written)")
     if not args.no_cpu_baseline:
         if isinstance(wl, StackWorkload):
             line["cpu_baseline"] = cpu_baseline_stack(args, wl)

@@ -203,6 +203,26 @@ int qlora_lora_grad(const uint16_t* x, const uint16_t* dy, int64_t M,
                     size_t ws_bytes, void* stream);
 
 /*
+ * Merge of the adapter into one dense bf16 weight for deployment: the LoRA
+ * update is low rank and folds back into the weights ("QLoRA"
+ * (techbytebybyte), "Curiosity question: is the final model permanently
+ * 4-bit?", "Training setup versus deployment setup"; figure 2 of "A 65B
+ * fine-tune on the GPU you already have"):
+ *     out = bf16( W' + (alpha / r) . B . A )      [N, K]
+ *   packed, qscale, step  the stored W [N, K]; N >= 1, K multiple of 64.
+ *   A [r, K], B [N, r] bf16 (NULL with r = 0: out is exactly
+ *           qlora_nf4_dequant's output); 1 <= r <= 128 otherwise.
+ *   out     [N, K] bf16, 16-byte aligned.
+ * W' is dequantized with the arithmetic of qlora_nf4_dequant; the rank-r sum
+ * is accumulated in fp32, scaled and added to W' with one fused multiply-add,
+ * then rounded to bf16 once. No workspace.
+ */
+int qlora_nf4_merge(const uint8_t* packed, const int8_t* qscale,
+                    const float* step, int64_t N, int64_t K,
+                    const uint16_t* A, const uint16_t* B, int r, float alpha,
+                    uint16_t* out, void* stream);
+
+/*
  * Host copy of the 16 fp32 levels and the 15 fp32 decision thresholds the
  * kernels use (host pointers). Derived once, in fp64, on first use.
  */

@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqlora_nf4.so")
 ARCH = "gfx950"
 
-SOURCES = ["codebook.cpp", "api.cpp", "quant.hip", "lora.hip", "small.hip", "gemm.hip", "grad.hip"]
+SOURCES = ["codebook.cpp", "api.cpp", "quant.hip", "lora.hip", "small.hip", "gemm.hip", "grad.hip", "merge.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -159,6 +159,21 @@ int qlora_nf4_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K, const 
                                         as_stream(stream)));
 }
 
+int qlora_nf4_merge(const uint8_t* packed, const int8_t* qscale, const float* step, int64_t N, int64_t K,
+                    const uint16_t* A, const uint16_t* B, int r, float alpha, uint16_t* out, void* stream) {
+  int st = check_weight(packed, qscale, step);
+  if (st) return st;
+  if (!out) return QLORA_ERR_NULL;
+  if (N < 1 || K < 64 || K % QLORA_BLOCK != 0 || N > (int64_t{1} << 24) || K > (int64_t{1} << 24))
+    return QLORA_ERR_SHAPE;
+  st = check_adapter(A, B, r);
+  if (st) return st;
+  if (!aligned16(out)) return QLORA_ERR_ALIGN;
+  const qnf4::Codebook* cb = qnf4::codebook();
+  if (!cb) return QLORA_ERR_INIT;
+  return hip_status(qnf4::launch_merge(packed, qscale, step, N, K, A, B, r, alpha, out, *cb, as_stream(stream)));
+}
+
 int qlora_lora_grad(const uint16_t* x, const uint16_t* dy, int64_t M, int64_t N, int64_t K, const uint16_t* A,
                     const uint16_t* B, int r, float alpha, float* dA, float* dB, int accumulate, void* workspace,
                     size_t ws_bytes, void* stream) {

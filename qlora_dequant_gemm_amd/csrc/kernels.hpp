@@ -143,6 +143,9 @@ hipError_t launch_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K, co
                          const int8_t* qscale, const float* step, const uint16_t* A, const uint16_t* B,
                          int r, float alpha, uint16_t* dx, void* ws, const Codebook& cb,
                          hipStream_t stream);
+hipError_t launch_merge(const uint8_t* packed, const int8_t* qscale, const float* step, int64_t N, int64_t K,
+                        const uint16_t* A, const uint16_t* B, int r, float alpha, uint16_t* out, const Codebook& cb,
+                        hipStream_t stream);
 hipError_t launch_lora_grad(const uint16_t* x, const uint16_t* dy, int64_t M, int64_t N, int64_t K,
                             const uint16_t* A, const uint16_t* B, int r, float alpha, float* dA, float* dB,
                             int accumulate, void* ws, hipStream_t stream);

@@ -204,6 +204,26 @@ def lora_grad(x, dy, A, B, alpha, dA=None, dB=None, accumulate=False, ws=None):
     return dA, dB
 
 
+def merge(qw, A=None, B=None, alpha=0.0, out=None):
+    """bf16 [N, K] = bf16(deq(W) + (alpha/r) . B . A): the adapter folded into one
+    dense weight (exactly the dequantized weight when there is no adapter)."""
+    N, K = qw.shape
+    r = 0 if A is None else A.shape[0]
+    if A is not None:
+        _need(A, torch.bfloat16, "A")
+        _need(B, torch.bfloat16, "B")
+        if tuple(A.shape) != (r, K) or tuple(B.shape) != (N, r):
+            raise ValueError("inconsistent adapter shapes")
+    dev = qw.packed.device
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    _need(out, torch.bfloat16, "out")
+    _lib.check("qlora_nf4_merge", _lib.lib().qlora_nf4_merge(
+        _ptr(qw.packed), _ptr(qw.qscale), _ptr(qw.step), N, K, _ptr(A), _ptr(B), r, float(alpha), _ptr(out),
+        _stream(dev)))
+    return out
+
+
 def codebook():
     """(levels[16], thresholds[15]) as the kernels use them, host floats."""
     L = (ctypes.c_float * 16)()

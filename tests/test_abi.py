@@ -132,6 +132,20 @@ def test_adapter_grad_rejects_bad_arguments(kwargs, status):
     assert _grad(**kwargs) == status
 
 
+@pytest.mark.parametrize("args,status", [
+    ((V(0), FAKE, FAKE, 16, 64, V(0), V(0), 0, 0.0, FAKE), 1),
+    ((FAKE, FAKE, FAKE, 16, 64, V(0), V(0), 0, 0.0, V(0)), 1),
+    ((FAKE, FAKE, FAKE, 0, 64, V(0), V(0), 0, 0.0, FAKE), 2),
+    ((FAKE, FAKE, FAKE, 16, 96, V(0), V(0), 0, 0.0, FAKE), 2),
+    ((FAKE, FAKE, FAKE, 16, 64, V(0), V(0), 0, 0.0, ODD), 3),
+    ((FAKE, FAKE, FAKE, 16, 64, FAKE, V(0), 4, 1.0, FAKE), 1),
+    ((FAKE, FAKE, FAKE, 16, 64, FAKE, FAKE, 129, 1.0, FAKE), 4),
+    ((FAKE, FAKE, FAKE, 16, 64, ODD, FAKE, 4, 1.0, FAKE), 3),
+])
+def test_merge_rejects_bad_arguments(args, status):
+    assert _lib.lib().qlora_nf4_merge(*args, V(0)) == status
+
+
 def test_quantize_dq_dequant_reject_bad_arguments():
     L = _lib.lib()
     assert L.qlora_nf4_quantize(V(0), 0, 64, FAKE, FAKE, V(0)) == 1

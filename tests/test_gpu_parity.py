@@ -578,3 +578,54 @@ def test_adapter_grad_full_size(qops, name):
     torch.cuda.empty_cache()
     oA, oB = gemm.lora_grads(inp["x"], inp["dy"], inp["A"], inp["B"], alpha, r)
     assert rel_fro(gA, oA) <= TIGHT and rel_fro(gB, oB) <= TIGHT
+
+
+# ---------------------------------------------------------------------------
+# merge of the adapter into one dense bf16 weight
+# ---------------------------------------------------------------------------
+def _merge_check(got_bits, ref, mag):
+    """Every entry within one bf16 ulp of the exact fp64 value plus the fp32
+    slack of the rank-r sum (2^-22 of mag = |W'| + s.|B|.|A|, which matters only
+    where W' and the update cancel); returns the fraction of entries that are
+    the exact value rounded to bf16 (within half an ulp)."""
+    got = to_f64(got_bits)
+    a = np.abs(ref)
+    ulp = np.where(a > 0, np.exp2(np.floor(np.log2(np.where(a > 0, a, 1.0))) - 7), 0.0)
+    assert np.all(np.abs(got - ref) <= ulp + 2.0 ** -22 * mag)
+    return float(np.mean(np.abs(got - ref) <= ulp / 2))
+
+
+def _merge_mag(wd, A, B, alpha, r):
+    return np.abs(to_f64(wd)) + (alpha / r) * (np.abs(to_f64(B)) @ np.abs(to_f64(A)))
+
+
+@pytest.mark.parametrize("N,K,r,alpha,seed", [(300, 320, 16, 32.0, 0), (37, 64, 5, 7.0, 1), (130, 1024, 64, 16.0, 2),
+                                              (8, 576, 128, 8.0, 3)])
+def test_merge_parity(qops, N, K, r, alpha, seed):
+    w = synth.weight(N, K, 800 + seed)
+    A, B = synth.adapters(N, K, r, 810 + seed, 820 + seed)
+    qw = gpu_quant(qops, w)
+    got = host_bits(qops.merge(qw, dev(A), dev(B), alpha))
+    opk, oq, ostep, _ = nf4.quantize_all(w)
+    wd = nf4.dequantize(opk, oq, ostep).reshape(N, K)
+    assert _merge_check(got, gemm.merge(wd, A, B, alpha, r), _merge_mag(wd, A, B, alpha, r)) >= 0.99
+
+
+def test_merge_without_adapter_is_dequant(qops):
+    w = synth.weight(300, 320, 830)
+    w[:, :64] = 0.0                                  # zero blocks dequantize to signed zeros
+    qw = gpu_quant(qops, w)
+    assert torch.equal(qops.merge(qw).view(torch.int16), qops.dequant(qw).view(torch.int16))
+
+
+def test_merge_full_size(qops):
+    inp = synth.config_inputs("7b_mlp_up", 1)
+    N, K, r, alpha = inp["N"], inp["K"], inp["r"], inp["alpha"]
+    qw = gpu_quant(qops, inp["w"])
+    got = host_bits(qops.merge(qw, dev(inp["A"]), dev(inp["B"]), alpha))
+    del qw
+    torch.cuda.empty_cache()
+    opk, oq, ostep, _ = nf4.quantize_all(inp["w"])
+    wd = nf4.dequantize(opk, oq, ostep).reshape(N, K)
+    mag = _merge_mag(wd, inp["A"], inp["B"], alpha, r)
+    assert _merge_check(got, gemm.merge(wd, inp["A"], inp["B"], alpha, r), mag) >= 0.99
