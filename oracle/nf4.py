@@ -123,8 +123,9 @@ def unpack(packed):
     return out
 
 
-def quantize(w):
-    """Block-wise NF4 quantization of a flat weight array.
+def quantize(w, levels=None):
+    """Block-wise NF4 quantization of a flat weight array (``levels``: another
+    16-level codebook, ascending, in [-1, 1]; see ``oracle.formats``).
 
     Accepts fp32 values, or bf16 given as uint16 bit patterns (widened to fp32
     exactly). Returns (packed uint8[numel/2], absmax fp32[numel/64]).
@@ -139,7 +140,7 @@ def quantize(w):
     chunk = 1 << 22                     # independent blocks, taken in slices
     for lo in range(0, w.size, chunk):  # only to bound the fp64 temporaries
         hi = min(lo + chunk, w.size)
-        codes = nearest_code(normalise(w[lo:hi], a[lo // BLOCK:hi // BLOCK]))
+        codes = nearest_code(normalise(w[lo:hi], a[lo // BLOCK:hi // BLOCK]), levels)
         packed[lo // 2:hi // 2] = pack(codes)
     return packed, a
 
@@ -190,13 +191,17 @@ def bf16_bits_to_f32(bits):
     return b.view(np.float32)
 
 
-def dequantize(packed, qscale, step, numel=None):
-    """NF4 + double-quantized constants -> bf16 bit patterns (uint16[numel])."""
+def dequantize(packed, qscale, step, numel=None, levels=None, absmax=None):
+    """NF4 + double-quantized constants -> bf16 bit patterns (uint16[numel]).
+
+    ``levels``: another codebook; ``absmax`` given (qscale, step None): the
+    block constants stored in fp32 without double quantization (s = absmax).
+    """
     codes = unpack(packed)
     if numel is not None:
         codes = codes[:numel]
-    L = codebook()
-    s = block_scales(qscale, step)
+    L = codebook() if levels is None else np.asarray(levels, dtype=np.float32)
+    s = np.asarray(absmax, dtype=np.float32) if absmax is not None else block_scales(qscale, step)
     blk = np.arange(codes.size) // BLOCK
     prod = (L[codes] * s[blk]).astype(np.float32)       # fp32 product
     return f32_to_bf16_bits(prod)
@@ -215,9 +220,9 @@ def dequantize_range(packed, qscale, step, lo, hi):
     return f32_to_bf16_bits(prod)
 
 
-def quantize_all(w):
+def quantize_all(w, levels=None):
     """Convenience: the full storage format (packed, qscale, step, absmax)."""
-    packed, absmax = quantize(w)
+    packed, absmax = quantize(w, levels)
     q, step = double_quantize(absmax)
     return packed, q, step, absmax
 
