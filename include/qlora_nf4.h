@@ -203,6 +203,37 @@ int qlora_lora_grad(const uint16_t* x, const uint16_t* dy, int64_t M,
                     size_t ws_bytes, void* stream);
 
 /*
+ * Other 16-level block formats, for comparison with NF4 ("QLoRA Explained",
+ * "The three ideas behind QLoRA": NF4 beats the standard 4-bit integer and
+ * float formats on normally distributed weights; figure 3 of "A 65B
+ * fine-tune on the GPU you already have": uniform bins), and storage without
+ * double quantization (4.5 bits per parameter, figure 4 of the same page).
+ *   format  QLORA_FMT_NF4 (the levels of qlora_nf4_quantize), QLORA_FMT_INT4
+ *           (the 16 evenly spaced levels (2i - 15) / 15) or QLORA_FMT_FP4 (the
+ *           E2M1 values 0, 0.5, 1, 1.5, 2, 3, 4, 6 over 6, signed; -0 and +0
+ *           are codes 7 and 8: v <= 0 codes -0, v > 0 codes +0); anything else
+ *           gives QLORA_ERR_DTYPE.
+ * Block size, absmax scaling, nearest-level rule, packing and double
+ * quantization are those of the NF4 calls. qlora_q4_quantize: qscale and step
+ * both NULL skips double quantization (the fp32 absmax is then the stored
+ * constant), both non-NULL double-quantizes in the same pass.
+ * qlora_q4_dequant: with qscale (and step) the constants are double-quantized
+ * as in qlora_nf4_dequant; with qscale NULL, s = absmax[b] directly. Outputs
+ * bf16 [numel]. The fused GEMMs take NF4 only.
+ */
+#define QLORA_FMT_NF4 0
+#define QLORA_FMT_INT4 1
+#define QLORA_FMT_FP4 2
+int qlora_q4_quantize(const void* w, int wdt, int64_t numel, int format,
+                      uint8_t* packed, float* absmax, int8_t* qscale,
+                      float* step, void* stream);
+int qlora_q4_dequant(const uint8_t* packed, const float* absmax,
+                     const int8_t* qscale, const float* step, int64_t numel,
+                     int format, uint16_t* out, void* stream);
+/* Host copy of a format's 16 fp32 levels and 15 thresholds. */
+int qlora_q4_codebook(int format, float levels[16], float thresholds[15]);
+
+/*
  * Merge of the adapter into one dense bf16 weight for deployment: the LoRA
  * update is low rank and folds back into the weights ("QLoRA"
  * (techbytebybyte), "Curiosity question: is the final model permanently

@@ -159,6 +159,42 @@ int qlora_nf4_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K, const 
                                         as_stream(stream)));
 }
 
+int qlora_q4_quantize(const void* w, int wdt, int64_t numel, int format, uint8_t* packed, float* absmax,
+                      int8_t* qscale, float* step, void* stream) {
+  if (!w || !packed || !absmax) return QLORA_ERR_NULL;
+  if ((qscale == nullptr) != (step == nullptr)) return QLORA_ERR_NULL;
+  if (wdt != QLORA_F32 && wdt != QLORA_BF16) return QLORA_ERR_DTYPE;
+  if (format < 0 || format >= qnf4::kNumFormats) return QLORA_ERR_DTYPE;
+  if (numel <= 0 || numel % QLORA_BLOCK != 0) return QLORA_ERR_SHAPE;
+  if (!aligned16(w) || !aligned16(packed)) return QLORA_ERR_ALIGN;
+  const qnf4::Codebook* cb = qnf4::codebook(format);
+  if (!cb) return QLORA_ERR_INIT;
+  return hip_status(qnf4::launch_quantize(w, wdt, numel, packed, absmax, qscale, step, *cb, as_stream(stream)));
+}
+
+int qlora_q4_dequant(const uint8_t* packed, const float* absmax, const int8_t* qscale, const float* step,
+                     int64_t numel, int format, uint16_t* out, void* stream) {
+  if (!packed || !out) return QLORA_ERR_NULL;
+  if (qscale ? !step : !absmax) return QLORA_ERR_NULL;
+  if (format < 0 || format >= qnf4::kNumFormats) return QLORA_ERR_DTYPE;
+  if (numel <= 0 || numel % QLORA_BLOCK != 0) return QLORA_ERR_SHAPE;
+  if (!aligned16(packed) || !aligned16(out)) return QLORA_ERR_ALIGN;
+  const qnf4::Codebook* cb = qnf4::codebook(format);
+  if (!cb) return QLORA_ERR_INIT;
+  return hip_status(qnf4::launch_dequant(packed, qscale, step, numel, out, *cb, as_stream(stream),
+                                         qscale ? nullptr : absmax));
+}
+
+int qlora_q4_codebook(int format, float levels[16], float thresholds[15]) {
+  if (!levels || !thresholds) return QLORA_ERR_NULL;
+  if (format < 0 || format >= qnf4::kNumFormats) return QLORA_ERR_DTYPE;
+  const qnf4::Codebook* cb = qnf4::codebook(format);
+  if (!cb) return QLORA_ERR_INIT;
+  for (int i = 0; i < 16; ++i) levels[i] = cb->L[i];
+  for (int i = 0; i < 15; ++i) thresholds[i] = cb->T[i];
+  return QLORA_OK;
+}
+
 int qlora_nf4_merge(const uint8_t* packed, const int8_t* qscale, const float* step, int64_t N, int64_t K,
                     const uint16_t* A, const uint16_t* B, int r, float alpha, uint16_t* out, void* stream) {
   int st = check_weight(packed, qscale, step);

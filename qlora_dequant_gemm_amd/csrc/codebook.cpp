@@ -13,6 +13,13 @@
 // fp32 that does not exceed the exact midpoint of levels j and j+1 (for an
 // fp32 v, v > RD(m) <=> v > m). The midpoint of two fp32 values in [-1, 1] is
 // exact in fp64.
+//
+// The other formats ("QLoRA Explained", "The three ideas behind QLoRA": NF4
+// beats the standard 4-bit integer and float formats on normal weights; "A 65B
+// fine-tune on the GPU you already have", figure 3): INT4 = the 16 evenly
+// spaced levels (2i - 15) / 15; FP4 = the E2M1 values 0, 0.5, 1, 1.5, 2, 3, 4, 6
+// divided by 6, with -0 and +0 as codes 7 and 8 (the threshold between them is
+// 0, so v <= 0 takes -0 and v > 0 takes +0).
 #include <cmath>
 #include <mutex>
 
@@ -51,45 +58,67 @@ float round_down_f32(double m) {
   return f;
 }
 
-Codebook g_cb;
-bool g_ok = false;
+Codebook g_cb[kNumFormats];
+bool g_ok[kNumFormats] = {false, false, false};
 std::once_flag g_once;
 
-void derive() {
-  // positive levels: probabilities (8.5 .. 15.5)/16, i.e. upper tails (7.5 .. 0.5)/16
-  double z[8];
-  for (int i = 0; i < 8; ++i) z[i] = upper_quantile((7.5 - i) / 16.0);
-  const double top = z[7];
+// positive half of each format's levels, fp64 (index 8 + i)
+void positive_levels(int format, double (&p)[8]) {
+  if (format == kNF4) {
+    // probabilities (8.5 .. 15.5)/16, i.e. upper tails (7.5 .. 0.5)/16
+    double z[8];
+    for (int i = 0; i < 8; ++i) z[i] = upper_quantile((7.5 - i) / 16.0);
+    for (int i = 0; i < 8; ++i) p[i] = z[i] / z[7];
+  } else if (format == kINT4) {
+    for (int i = 0; i < 8; ++i) p[i] = (2.0 * (8 + i) - 15.0) / 15.0;
+  } else {
+    const double e2m1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    for (int i = 0; i < 8; ++i) p[i] = e2m1[i] / 6.0;
+  }
+}
+
+bool derive_one(int format, Codebook& cb) {
+  double p[8];
+  positive_levels(format, p);
   for (int i = 0; i < 8; ++i) {
-    float v = static_cast<float>(z[i] / top);
-    g_cb.L[8 + i] = v;
-    g_cb.L[7 - i] = -v;
+    const float v = static_cast<float>(p[i]);
+    cb.L[8 + i] = v;
+    cb.L[7 - i] = -v;                          // exact negation (FP4: -0 at 7)
   }
   for (int j = 0; j < 15; ++j) {
-    double m = (static_cast<double>(g_cb.L[j]) + static_cast<double>(g_cb.L[j + 1])) / 2.0;
-    g_cb.T[j] = round_down_f32(m);
+    double m = (static_cast<double>(cb.L[j]) + static_cast<double>(cb.L[j + 1])) / 2.0;
+    cb.T[j] = round_down_f32(m);
+    if (cb.T[j] == 0.0f) cb.T[j] = 0.0f;       // +0
   }
-  g_cb.pad = 0.0f;
-  bool ok = g_cb.L[0] == -1.0f && g_cb.L[15] == 1.0f;
-  for (int j = 0; j < 15; ++j) ok = ok && g_cb.L[j] < g_cb.L[j + 1] && g_cb.T[j] >= g_cb.L[j] && g_cb.T[j] < g_cb.L[j + 1];
+  cb.pad = 0.0f;
+  bool ok = cb.L[0] == -1.0f && cb.L[15] == 1.0f;
+  for (int j = 0; j < 15; ++j) {
+    const bool zeros = cb.L[j] == 0.0f && cb.L[j + 1] == 0.0f && std::signbit(cb.L[j]) && !std::signbit(cb.L[j + 1]);
+    ok = ok && (cb.L[j] < cb.L[j + 1] || zeros) && cb.T[j] >= cb.L[j] && (cb.T[j] < cb.L[j + 1] || zeros);
+  }
   // The quantize kernel's cell lookup (cell(v) = floor(64 v + 64.5)) needs
   // every threshold well inside its cell and at most one threshold per cell.
   int prev_cell = -1;
   for (int j = 0; j < 15; ++j) {
-    const double pos = static_cast<double>(g_cb.T[j]) * 64.0 + 64.5;
+    const double pos = static_cast<double>(cb.T[j]) * 64.0 + 64.5;
     const double frac = pos - std::floor(pos);
     const int cell = static_cast<int>(std::floor(pos));
     ok = ok && frac > 64.0 * kCellMargin && frac < 1.0 - 64.0 * kCellMargin && cell > prev_cell;
     prev_cell = cell;
   }
-  g_ok = ok;
+  return ok;
+}
+
+void derive() {
+  for (int f = 0; f < kNumFormats; ++f) g_ok[f] = derive_one(f, g_cb[f]);
 }
 
 }  // namespace
 
-const Codebook* codebook() {
+const Codebook* codebook(int format) {
+  if (format < 0 || format >= kNumFormats) return nullptr;
   std::call_once(g_once, derive);
-  return g_ok ? &g_cb : nullptr;
+  return g_ok[format] ? &g_cb[format] : nullptr;
 }
 
 }  // namespace qnf4

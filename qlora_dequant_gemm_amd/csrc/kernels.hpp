@@ -115,8 +115,9 @@ hipError_t launch_quantize(const void* w, int wdt, int64_t numel, uint8_t* packe
                            int8_t* qscale, float* step, const Codebook& cb, hipStream_t stream);
 hipError_t launch_dq_scales(const float* absmax, int64_t nblocks, int8_t* qscale, float* step,
                             hipStream_t stream);
+// qscale == NULL: the constants are the fp32 absmax values (no double quantization)
 hipError_t launch_dequant(const uint8_t* packed, const int8_t* qscale, const float* step, int64_t numel,
-                          uint16_t* out, const Codebook& cb, hipStream_t stream);
+                          uint16_t* out, const Codebook& cb, hipStream_t stream, const float* absmax = nullptr);
 
 // rank-r down projection of `in` [M][Kc] by the adapter (wrow: A [r][Kc];
 // else B [Kc][r]); M <= kSmallM (ldt == 0) writes lora_splits fp32 partials,

@@ -276,15 +276,18 @@ __global__ __launch_bounds__(256) void k_dq_scales(const float* __restrict__ abs
 // k_dequant: each lane turns 16 packed bytes (32 codes, half a block) into
 // 32 bf16 (64 bytes).
 // ---------------------------------------------------------------------------
+// DQ == false: the block constants are the fp32 absmax values themselves
+// (storage without double quantization).
+template <bool DQ>
 __global__ __launch_bounds__(256) void k_dequant(const u32x4* __restrict__ packed, const int8_t* __restrict__ qscale,
-                                                 const float* __restrict__ step, int64_t nchunks,
-                                                 u32x4* __restrict__ out, Codebook cb) {
+                                                 const float* __restrict__ step, const float* __restrict__ absmax,
+                                                 int64_t nchunks, u32x4* __restrict__ out, Codebook cb) {
   const int64_t first = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t c = first; c < nchunks; c += stride) {
     const u32x4 p = packed[c];
     const int64_t blk = c >> 1;                // 2 chunks of 32 codes per block
-    const float s = block_scale(qscale[blk], step[blk >> 8]);
+    const float s = DQ ? block_scale(qscale[blk], step[blk >> 8]) : absmax[blk];
     const MagTable t = make_table(cb, s);
     out[c * 4 + 0] = decode8(p.x, t);
     out[c * 4 + 1] = decode8(p.y, t);
@@ -343,11 +346,15 @@ hipError_t launch_dq_scales(const float* absmax, int64_t nblocks, int8_t* qscale
 }
 
 hipError_t launch_dequant(const uint8_t* packed, const int8_t* qscale, const float* step, int64_t numel,
-                          uint16_t* out, const Codebook& cb, hipStream_t stream) {
+                          uint16_t* out, const Codebook& cb, hipStream_t stream, const float* absmax) {
   const int64_t nchunks = numel / 32;
   const int grid = grid_for(nchunks, 256);
-  hipLaunchKernelGGL(k_dequant, dim3(grid), dim3(256), 0, stream, reinterpret_cast<const u32x4*>(packed),
-                     qscale, step, nchunks, reinterpret_cast<u32x4*>(out), cb);
+  if (qscale)
+    hipLaunchKernelGGL(k_dequant<true>, dim3(grid), dim3(256), 0, stream, reinterpret_cast<const u32x4*>(packed),
+                       qscale, step, nullptr, nchunks, reinterpret_cast<u32x4*>(out), cb);
+  else
+    hipLaunchKernelGGL(k_dequant<false>, dim3(grid), dim3(256), 0, stream, reinterpret_cast<const u32x4*>(packed),
+                       nullptr, nullptr, absmax, nchunks, reinterpret_cast<u32x4*>(out), cb);
   return hipGetLastError();
 }
 

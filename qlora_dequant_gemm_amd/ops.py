@@ -204,6 +204,48 @@ def lora_grad(x, dy, A, B, alpha, dA=None, dB=None, accumulate=False, ws=None):
     return dA, dB
 
 
+NF4, INT4, FP4 = 0, 1, 2
+
+
+def q4_quantize(w, fmt, double_quant=True):
+    """Block-64 quantization in another 16-level format (NF4, INT4 or FP4):
+    (packed, absmax, qscale, step), qscale/step None without double quantization."""
+    if w.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("weight must be float32 or bfloat16")
+    _need(w, w.dtype, "w")
+    numel = w.numel()
+    nb = numel // BLOCK
+    dev = w.device
+    packed = torch.empty(numel // 2, dtype=torch.uint8, device=dev)
+    absmax = torch.empty(nb, dtype=torch.float32, device=dev)
+    q = torch.empty(nb, dtype=torch.int8, device=dev) if double_quant else None
+    step = torch.empty((nb + DQ_GROUP - 1) // DQ_GROUP, dtype=torch.float32, device=dev) if double_quant else None
+    wdt = _lib.F32 if w.dtype == torch.float32 else _lib.BF16
+    _lib.check("qlora_q4_quantize", _lib.lib().qlora_q4_quantize(
+        _ptr(w), wdt, numel, int(fmt), _ptr(packed), _ptr(absmax), _ptr(q), _ptr(step), _stream(dev)))
+    return packed, absmax, q, step
+
+
+def q4_dequant(packed, fmt, absmax=None, qscale=None, step=None, out=None):
+    """bf16 [numel] from a block-64 format; double-quantized constants when
+    qscale/step are given, else the fp32 absmax."""
+    numel = packed.numel() * 2
+    dev = packed.device
+    if out is None:
+        out = torch.empty(numel, dtype=torch.bfloat16, device=dev)
+    _need(out, torch.bfloat16, "out")
+    _lib.check("qlora_q4_dequant", _lib.lib().qlora_q4_dequant(
+        _ptr(packed), _ptr(absmax), _ptr(qscale), _ptr(step), numel, int(fmt), _ptr(out), _stream(dev)))
+    return out
+
+
+def q4_codebook(fmt):
+    L = (ctypes.c_float * 16)()
+    T = (ctypes.c_float * 15)()
+    _lib.check("qlora_q4_codebook", _lib.lib().qlora_q4_codebook(int(fmt), L, T))
+    return list(L), list(T)
+
+
 def merge(qw, A=None, B=None, alpha=0.0, out=None):
     """bf16 [N, K] = bf16(deq(W) + (alpha/r) . B . A): the adapter folded into one
     dense weight (exactly the dequantized weight when there is no adapter)."""

@@ -50,6 +50,33 @@ def test_codebook_bitwise_equals_oracle():
     assert np.all(np.nextafter(T, np.float32(2)).astype(np.float64) > mids)
 
 
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_format_codebooks_bitwise_equal_oracle(fmt):
+    from oracle import formats
+    levels, thresholds = ops.q4_codebook(fmt)
+    L = np.array(levels, np.float32)
+    assert np.array_equal(L.view(np.uint32), formats.levels(fmt).view(np.uint32))
+    mids = nf4.level_midpoints(formats.levels(fmt))
+    T = np.array(thresholds, np.float32)
+    assert np.all(T.astype(np.float64) <= mids)
+    assert np.all(np.nextafter(T, np.float32(2)).astype(np.float64) > mids)
+
+
+def test_format_calls_reject_bad_arguments():
+    L = _lib.lib()
+    a = (ctypes.c_float * 16)()
+    b = (ctypes.c_float * 15)()
+    assert L.qlora_q4_codebook(3, a, b) == 6 and L.qlora_q4_codebook(-1, a, b) == 6
+    assert L.qlora_q4_quantize(FAKE, 0, 64, 3, FAKE, FAKE, V(0), V(0), V(0)) == 6
+    assert L.qlora_q4_quantize(FAKE, 0, 64, 1, FAKE, FAKE, FAKE, V(0), V(0)) == 1
+    assert L.qlora_q4_quantize(FAKE, 0, 96, 1, FAKE, FAKE, V(0), V(0), V(0)) == 2
+    assert L.qlora_q4_quantize(ODD, 0, 64, 1, FAKE, FAKE, V(0), V(0), V(0)) == 3
+    assert L.qlora_q4_dequant(FAKE, V(0), V(0), V(0), 64, 1, FAKE, V(0)) == 1
+    assert L.qlora_q4_dequant(FAKE, V(0), FAKE, V(0), 64, 1, FAKE, V(0)) == 1
+    assert L.qlora_q4_dequant(FAKE, FAKE, V(0), V(0), 64, 5, FAKE, V(0)) == 6
+    assert L.qlora_q4_dequant(FAKE, FAKE, V(0), V(0), 65, 2, FAKE, V(0)) == 2
+
+
 def test_workspace_sizes():
     ws = ops.workspace_bytes
     assert ws(0, 4096, 11008, 4096, 0) == 0

@@ -96,10 +96,11 @@ def test_exact_level_weights_code_to_themselves(qops):
     assert np.array_equal(nf4.unpack(packed.cpu().numpy()), c.astype(np.uint8))
 
 
-def _near_threshold_weights():
+def _near_threshold_weights(levels=None):
     """Blocks whose absmax is 1, so w / absmax = w exactly: every threshold,
     its fp32 neighbours and the levels themselves, in both signs."""
-    L = nf4.codebook().astype(np.float64)
+    levels = nf4.codebook() if levels is None else levels
+    L = levels.astype(np.float64)
     vals = []
     for j in range(15):
         m = np.float32((L[j] + L[j + 1]) / 2)
@@ -109,7 +110,7 @@ def _near_threshold_weights():
         for _ in range(7):
             vals.append(x)
             x = np.nextafter(x, np.float32(2))
-    vals += list(nf4.codebook()) + [np.float32(0.0), np.float32(-0.0), np.float32(1e-9), np.float32(-1e-9)]
+    vals += list(levels) + [np.float32(0.0), np.float32(-0.0), np.float32(1e-9), np.float32(-1e-9)]
     vals = np.array(vals, np.float32)
     n = 63 * ((vals.size + 62) // 63)
     vals = np.resize(vals, n).reshape(-1, 63)
@@ -629,3 +630,58 @@ def test_merge_full_size(qops):
     wd = nf4.dequantize(opk, oq, ostep).reshape(N, K)
     mag = _merge_mag(wd, inp["A"], inp["B"], alpha, r)
     assert _merge_check(got, gemm.merge(wd, inp["A"], inp["B"], alpha, r), mag) >= 0.99
+
+
+
+# ---------------------------------------------------------------------------
+# other 16-level formats (INT4, FP4) and storage without double quantization
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_format_quantize_dequant_bit_exact(qops, fmt):
+    from oracle import formats
+    L = formats.levels(fmt)
+    near = _near_threshold_weights(L)
+    w = np.concatenate([near, np.zeros(64, np.float32),                       # and an all-zero block
+                        synth.weight(300, 320, 900 + fmt).reshape(-1)])
+    w = np.concatenate([w, synth.weight(1, 64 * (-(w.size // 64) % 256 + 3), 910).reshape(-1)])
+    wt = dev(w)
+    for dq in (True, False):
+        packed, absmax, q, step = qops.q4_quantize(wt, fmt, double_quant=dq)
+        opk, oa = nf4.quantize(w, L)
+        assert np.array_equal(packed.cpu().numpy(), opk)
+        assert np.array_equal(absmax.cpu().numpy().view(np.uint32), oa.view(np.uint32))
+        if dq:
+            oq, ostep = nf4.double_quantize(oa)
+            assert np.array_equal(q.cpu().numpy(), oq)
+            assert np.array_equal(step.cpu().numpy().view(np.uint32), ostep.view(np.uint32))
+            got = host_bits(qops.q4_dequant(packed, fmt, qscale=q, step=step))
+            assert np.array_equal(got, nf4.dequantize(opk, oq, ostep, levels=L))
+        else:
+            got = host_bits(qops.q4_dequant(packed, fmt, absmax=absmax))
+            assert np.array_equal(got, nf4.dequantize(opk, None, None, levels=L, absmax=oa))
+
+
+def test_format_nf4_call_equals_nf4_entry_points(qops):
+    w = dev(synth.weight(256, 512, 920))
+    packed, absmax, q, step = qops.q4_quantize(w, 0)
+    qw = qops.quantize_weight(w)
+    assert torch.equal(packed, qw.packed) and torch.equal(q, qw.qscale) and torch.equal(step, qw.step)
+    assert torch.equal(qops.q4_dequant(packed, 0, qscale=q, step=step).view(torch.int16),
+                       qops.dequant(qw).reshape(-1).view(torch.int16))
+
+
+def test_format_error_ordering_on_7b_weight(qops):
+    """The pages' claim on the 7B attention weight (N(0, 0.02)), from the GPU's
+    own stored formats: NF4 has the smallest reconstruction error, with and
+    without double quantization."""
+    c = synth.CONFIGS["7b_attn"]
+    w = dev(synth.weight(c["N"], c["K"], c["seeds"]["w"]))
+    err = {}
+    for fmt in (0, 1, 2):
+        for dq in (True, False):
+            packed, absmax, q, step = qops.q4_quantize(w, fmt, double_quant=dq)
+            d = qops.q4_dequant(packed, fmt, absmax=absmax, qscale=q, step=step).float().reshape(w.shape)
+            err[fmt, dq] = (torch.linalg.norm(d - w) / torch.linalg.norm(w)).item()
+    print({f"{['nf4', 'int4', 'fp4'][f]}{'' if dq else '_nodq'}": round(e, 5) for (f, dq), e in err.items()})
+    for dq in (True, False):
+        assert err[0, dq] < err[1, dq] and err[0, dq] < err[2, dq]
