@@ -160,10 +160,20 @@ class Workload:
         return [(lab, [self.calls(c)[i][1] for c in range(self.C)]) for i, lab in enumerate(labels)]
 
     def extra_groups(self):
-        """Calls timed beside the step but not part of it: the adapter gradients
-        (training shapes only)."""
+        """Calls timed beside the step but not part of it: decode shapes, the
+        grouped forward of three weights sharing x (q, k, v of a layer); training
+        shapes, the adapter gradients and the merge."""
         if self.decode:
-            return []
+            out = []
+            N, K, r = self.N, self.K, self.r
+            for M in self.Ms:
+                fns = [lambda c=c, M=M: self.ops.lora_fwd_grouped(self.x[M], [self.qw[(c + i) % self.C] for i in range(3)],
+                                                                  [self.A] * 3, [self.B] * 3, self.alpha, ws=self.ws)
+                       for c in range(0, self.C, 3)]
+                byts = 3 * (N * K * NF4_BYTES_PER_PARAM + 2 * r * (K + N) + 2 * M * N) + 2 * M * K
+                out.append((f"fwd_qkv_grouped_M{M}", fns, (byts, 3 * matmul_flops(M, N, K, r))))
+            self.ws.get(3 * self.ops.workspace_bytes(0, max(self.Ms), N, K, r))
+            return out
         M = max(self.Ms)
         N, K, r = self.N, self.K, self.r
         dev = "cuda"
@@ -563,8 +573,10 @@ def main():
         "step_bytes": step_bytes, "step_flops": step_flops,
     }
     if wl.extra:
-        line["outside_step"] = dict(wl.extra, note="timed alone at the step's shapes: adapter gradients dA, "
-                                                   "dB (qlora_lora_grad; GB/s counts x and dY read once and "
+        line["outside_step"] = dict(wl.extra, note="timed alone at the step's shapes: decode, one grouped "
+                                                   "forward of three weights sharing x (qlora_nf4_lora_fwd_"
+                                                   "grouped); training, adapter gradients dA, dB "
+                                                   "(qlora_lora_grad; GB/s counts x and dY read once and "
                                                    "dA, dB written) and the adapter merged into one bf16 "
                                                    "weight (qlora_nf4_merge; NF4 read + bf16 written)")
     if not args.no_cpu_baseline:

@@ -156,6 +156,31 @@ int qlora_nf4_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K,
                        size_t ws_bytes, void* stream);
 
 /*
+ * Forward of several QLoRA linears that share their input (e.g. the q, k and
+ * v projections of one layer), as qlora_nf4_lora_fwd on each weight i:
+ *     y[i] = bf16( x . W_i'^T + (alpha / r) . bf16(x . A_i^T) . B_i^T )
+ * For M <= 16 the weights are streamed by one launch (their down-projections
+ * first), so the launch ramp is paid once; larger M runs the tiled forward
+ * per weight. Results are bitwise those of the single call.
+ *   x        [M, K] bf16 (device); G in 1..8.
+ *   packed, qscale, step, N, A, B, y  host arrays of G entries: the device
+ *            pointers of weight i's stored format (N[i] rows), its adapters
+ *            ([r, K] and [N[i], r]; the arrays A and B may be NULL with
+ *            r = 0) and its output y[i] [M, N[i]].
+ *   workspace / ws_bytes  at least G * qlora_workspace_bytes(0, M, max N, K, r).
+ * Alignment and size limits as in qlora_nf4_lora_fwd. Only the launch is
+ * shared, not the arithmetic.
+ */
+int qlora_nf4_lora_fwd_grouped(const uint16_t* x, int64_t M, int64_t K, int G,
+                               const uint8_t* const* packed,
+                               const int8_t* const* qscale,
+                               const float* const* step, const int64_t* N,
+                               const uint16_t* const* A,
+                               const uint16_t* const* B, int r, float alpha,
+                               uint16_t* const* y, void* workspace,
+                               size_t ws_bytes, void* stream);
+
+/*
  * Backward to the input through the frozen dequantized weight (figure 2 of
  * "A 65B fine-tune on the GPU you already have": gradients flow through the
  * frozen 4-bit weights into the adapters; "QLoRA" (techbytebybyte), "Follow

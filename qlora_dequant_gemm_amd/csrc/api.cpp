@@ -140,6 +140,37 @@ int qlora_nf4_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K, const
                                           as_stream(stream)));
 }
 
+int qlora_nf4_lora_fwd_grouped(const uint16_t* x, int64_t M, int64_t K, int G, const uint8_t* const* packed,
+                               const int8_t* const* qscale, const float* const* step, const int64_t* N,
+                               const uint16_t* const* A, const uint16_t* const* B, int r, float alpha,
+                               uint16_t* const* y, void* workspace, size_t ws_bytes, void* stream) {
+  if (!x || !packed || !qscale || !step || !N || !y) return QLORA_ERR_NULL;
+  if (G < 1 || G > qnf4::kMaxGroups) return QLORA_ERR_SHAPE;
+  if (M < 1 || K < 64 || K % QLORA_BLOCK != 0 || M > (int64_t{1} << 31) || K > (int64_t{1} << 24))
+    return QLORA_ERR_SHAPE;
+  if (r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_RANK;
+  if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
+  if (!aligned16(x)) return QLORA_ERR_ALIGN;
+  int64_t nmax = 0;
+  for (int i = 0; i < G; ++i) {
+    int st = check_weight(packed[i], qscale[i], step[i]);
+    if (st) return st;
+    if (!y[i]) return QLORA_ERR_NULL;
+    if (N[i] < 1 || N[i] > (int64_t{1} << 24)) return QLORA_ERR_SHAPE;
+    if (!aligned16(y[i])) return QLORA_ERR_ALIGN;
+    st = check_adapter(r ? A[i] : nullptr, r ? B[i] : nullptr, r);
+    if (st) return st;
+    nmax = N[i] > nmax ? N[i] : nmax;
+  }
+  const size_t per = qnf4::ws_layout(0, M, nmax, K, r).total;
+  const int st = check_ws(workspace, ws_bytes, per * static_cast<size_t>(G));
+  if (st) return st;
+  const qnf4::Codebook* cb = qnf4::codebook();
+  if (!cb) return QLORA_ERR_INIT;
+  return hip_status(qnf4::launch_lora_fwd_grouped(x, M, K, G, packed, qscale, step, N, A, B, r, alpha, y, workspace,
+                                                  per, *cb, as_stream(stream)));
+}
+
 int qlora_nf4_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
                      const int8_t* qscale, const float* step, const uint16_t* A, const uint16_t* B, int r,
                      float alpha, uint16_t* dx, void* workspace, size_t ws_bytes, void* stream) {

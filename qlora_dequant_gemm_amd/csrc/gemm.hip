@@ -736,6 +736,42 @@ hipError_t launch_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K, c
   return hipGetLastError();
 }
 
+// Weights sharing x: decode shapes compute every weight's t, then run one
+// grouped GEMV launch; larger M runs the tiled forward per weight (launch
+// overhead is negligible there). per_group_ws: bytes of workspace per weight.
+hipError_t launch_lora_fwd_grouped(const uint16_t* x, int64_t M, int64_t K, int G, const uint8_t* const* packed,
+                                   const int8_t* const* qscale, const float* const* step, const int64_t* N,
+                                   const uint16_t* const* A, const uint16_t* const* B, int r, float alpha,
+                                   uint16_t* const* y, void* ws, size_t per_group_ws, const Codebook& cb,
+                                   hipStream_t stream) {
+  char* wsb = static_cast<char*>(ws);
+  if (M > kSmallM) {
+    for (int i = 0; i < G; ++i) {
+      const hipError_t e = launch_lora_fwd(x, M, N[i], K, packed[i], qscale[i], step[i], r ? A[i] : nullptr,
+                                           r ? B[i] : nullptr, r, alpha, y[i], ws, cb, stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
+  const int rp = r > 0 ? static_cast<int>(rank_pad(r)) : 0;
+  GemvGroups grp{};
+  grp.count = G;
+  int64_t wg = 0;
+  for (int i = 0; i < G; ++i) {
+    float* tpart = nullptr;
+    if (r > 0) {
+      const WsLayout L = ws_layout(0, M, N[i], K, r);
+      tpart = reinterpret_cast<float*>(wsb + i * per_group_ws + L.lora_off);
+      const hipError_t e = launch_lora_down(true, x, M, K, A[i], r, tpart, stream, nullptr, nullptr);
+      if (e != hipSuccess) return e;
+    }
+    grp.g[i] = GemvGroup{packed[i], qscale[i], step[i], tpart, r ? B[i] : nullptr, y[i], N[i], wg};
+    wg += cdiv(N[i], 16);
+  }
+  return launch_fwd_small_grouped(x, M, K, grp, static_cast<int>(lora_splits(M, K)), rp, r, scale, cb, stream);
+}
+
 hipError_t launch_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
                          const int8_t* qscale, const float* step, const uint16_t* A, const uint16_t* B,
                          int r, float alpha, uint16_t* dx, void* ws, const Codebook& cb,

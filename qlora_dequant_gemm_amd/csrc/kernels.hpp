@@ -131,6 +131,29 @@ hipError_t launch_fwd_small(const uint16_t* x, int64_t M, int64_t N, int64_t K, 
                             const int8_t* qscale, const float* step, const float* tpart, int St, int rp,
                             const uint16_t* B, int r, float scale, uint16_t* y, const Codebook& cb,
                             hipStream_t stream);
+// Grouped decode forward: up to kMaxGroups weights sharing x in one launch.
+constexpr int kMaxGroups = 8;
+struct GemvGroup {
+  const uint8_t* packed;
+  const int8_t* qscale;
+  const float* step;
+  const float* tpart;          // this weight's t partial sums (fp32 [St][M][rp])
+  const uint16_t* B;
+  uint16_t* y;
+  int64_t N;
+  int64_t wg0;                 // first workgroup of this weight
+};
+struct GemvGroups {
+  GemvGroup g[kMaxGroups];
+  int count;
+};
+hipError_t launch_fwd_small_grouped(const uint16_t* x, int64_t M, int64_t K, const GemvGroups& G, int St, int rp,
+                                    int r, float scale, const Codebook& cb, hipStream_t stream);
+hipError_t launch_lora_fwd_grouped(const uint16_t* x, int64_t M, int64_t K, int G, const uint8_t* const* packed,
+                                   const int8_t* const* qscale, const float* const* step, const int64_t* N,
+                                   const uint16_t* const* A, const uint16_t* const* B, int r, float alpha,
+                                   uint16_t* const* y, void* ws, size_t per_group_ws, const Codebook& cb,
+                                   hipStream_t stream);
 hipError_t launch_bwd_small(const uint16_t* dy, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
                             const int8_t* qscale, const float* step, float* upart, int rp, const uint16_t* A,
                             const uint16_t* B, int r, float scale, float* part, uint16_t* dx, const Codebook& cb,

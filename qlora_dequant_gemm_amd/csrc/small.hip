@@ -35,18 +35,19 @@ struct GemvStage {
 // ---------------------------------------------------------------------------
 constexpr int kGemvWaves = 16;
 
-__global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_fwd(const uint16_t* __restrict__ x, int64_t M, int64_t N,
-                                                  int64_t K, const uint8_t* __restrict__ packed,
-                                                  const int8_t* __restrict__ qscale,
-                                                  const float* __restrict__ step,
-                                                  const float* __restrict__ tpart, int St, int rp,
-                                                  const uint16_t* __restrict__ Bl, int r, float scale,
-                                                  uint16_t* __restrict__ y, Codebook cb) {
+// The body of one workgroup (weight rows n0 .. n0 + 15); the plain kernel and
+// the grouped one (several weights sharing x) differ only in how a workgroup
+// finds its weight and rows.
+__device__ __forceinline__ void gemv_fwd_rows(const uint16_t* __restrict__ x, int64_t M, int64_t N, int64_t K,
+                                              const uint8_t* __restrict__ packed,
+                                              const int8_t* __restrict__ qscale, const float* __restrict__ step,
+                                              const float* __restrict__ tpart, int St, int rp,
+                                              const uint16_t* __restrict__ Bl, int r, float scale,
+                                              uint16_t* __restrict__ y, const Codebook& cb, int64_t n0) {
   __shared__ f32x4 red[kGemvWaves][64];
   extern __shared__ f32x4 tred[];            // [wave][js][lane][2]
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
   const int64_t n = imin(n0 + c, N - 1);
   const int64_t m = imin(static_cast<int64_t>(c), M - 1);
   const int64_t nbr = K / 64;
@@ -150,6 +151,31 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_fwd(const uint16_t* __
     const int64_t mm = 4 * g + v;
     if (mm < M && nn < N) y[mm * N + nn] = bf16_bits(acc[v]);
   }
+}
+
+__global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_fwd(const uint16_t* __restrict__ x, int64_t M, int64_t N,
+                                                  int64_t K, const uint8_t* __restrict__ packed,
+                                                  const int8_t* __restrict__ qscale,
+                                                  const float* __restrict__ step,
+                                                  const float* __restrict__ tpart, int St, int rp,
+                                                  const uint16_t* __restrict__ Bl, int r, float scale,
+                                                  uint16_t* __restrict__ y, Codebook cb) {
+  gemv_fwd_rows(x, M, N, K, packed, qscale, step, tpart, St, rp, Bl, r, scale, y, cb,
+                static_cast<int64_t>(blockIdx.x) * 16);
+}
+
+// Several weights that share x (e.g. the q, k, v projections) in one launch:
+// workgroups [wg0_i, wg0_{i+1}) take weight i's rows 16 at a time.
+__global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_fwd_grouped(const uint16_t* __restrict__ x, int64_t M,
+                                                          int64_t K, int St, int rp, int r, float scale,
+                                                          Codebook cb, GemvGroups G) {
+  int gi = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGroups; ++i)
+    if (i < G.count && static_cast<int64_t>(blockIdx.x) >= G.g[i].wg0) gi = i;
+  const GemvGroup& q = G.g[gi];
+  gemv_fwd_rows(x, M, q.N, K, q.packed, q.qscale, q.step, q.tpart, St, rp, q.B, r, scale, q.y, cb,
+                (static_cast<int64_t>(blockIdx.x) - q.wg0) * 16);
 }
 
 // ---------------------------------------------------------------------------
@@ -364,6 +390,16 @@ hipError_t launch_fwd_small(const uint16_t* x, int64_t M, int64_t N, int64_t K, 
   hipLaunchKernelGGL(k_gemv_fwd, dim3(static_cast<unsigned>(cdiv(N, 16))), dim3(64 * kGemvWaves), lds, stream, x, M,
                      N, K,
                      packed, qscale, step, tpart, St, rp, B, r, scale, y, cb);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_small_grouped(const uint16_t* x, int64_t M, int64_t K, const GemvGroups& G, int St, int rp,
+                                    int r, float scale, const Codebook& cb, hipStream_t stream) {
+  const size_t lds = r > 0 ? static_cast<size_t>(rp / 32) * kGemvWaves * 64 * 32 : 0;
+  int64_t wgs = 0;
+  for (int i = 0; i < G.count; ++i) wgs += cdiv(G.g[i].N, 16);
+  hipLaunchKernelGGL(k_gemv_fwd_grouped, dim3(static_cast<unsigned>(wgs)), dim3(64 * kGemvWaves), lds, stream, x, M,
+                     K, St, rp, r, scale, cb, G);
   return hipGetLastError();
 }
 

@@ -158,6 +158,26 @@ def lora_fwd(x, qw, A=None, B=None, alpha=0.0, out=None, ws=None):
     return out
 
 
+def lora_fwd_grouped(x, qws, As=None, Bs=None, alpha=0.0, outs=None, ws=None):
+    """The forward of several weights sharing x (one launch for M <= 16):
+    returns [x . deq(W_i)^T + (alpha/r) . (x . A_i^T) . B_i^T for each i]."""
+    _need(x, torch.bfloat16, "x")
+    M, K = x.shape
+    G = len(qws)
+    r = 0 if As is None else As[0].shape[0]
+    Ns = [qw.shape[0] for qw in qws]
+    if outs is None:
+        outs = [torch.empty((M, n), dtype=torch.bfloat16, device=x.device) for n in Ns]
+    arr = lambda ts: (ctypes.c_void_p * G)(*[t.data_ptr() if t is not None else 0 for t in ts])
+    need = G * workspace_bytes(0, M, max(Ns), K, r)
+    wsb = (ws or Workspace(x.device)).get(need)
+    _lib.check("qlora_nf4_lora_fwd_grouped", _lib.lib().qlora_nf4_lora_fwd_grouped(
+        _ptr(x), M, K, G, arr([q.packed for q in qws]), arr([q.qscale for q in qws]), arr([q.step for q in qws]),
+        (ctypes.c_int64 * G)(*Ns), arr(As) if r else None, arr(Bs) if r else None, r, float(alpha), arr(outs),
+        _ptr(wsb), 0 if wsb is None else wsb.numel(), _stream(x.device)))
+    return outs
+
+
 def bwd_dx(dy, qw, A=None, B=None, alpha=0.0, out=None, ws=None):
     """dX = dY . deq(W) + (alpha/r) . (dY . B) . A, bf16 [M, N] -> [M, K]."""
     _need(dy, torch.bfloat16, "dy")

@@ -173,6 +173,24 @@ def test_merge_rejects_bad_arguments(args, status):
     assert _lib.lib().qlora_nf4_merge(*args, V(0)) == status
 
 
+def test_grouped_forward_rejects_bad_arguments():
+    L = _lib.lib()
+    P = lambda *v: (ctypes.c_void_p * len(v))(*v)
+    N = lambda *v: (ctypes.c_int64 * len(v))(*v)
+    f, o = 0x10000, 0x10008
+    ok = dict(x=FAKE, M=4, K=64, G=2, pk=P(f, f), q=P(f, f), st=P(f, f), n=N(64, 32), A=None, B=None, r=0,
+              y=P(f, f), ws=V(0), wsb=0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.qlora_nf4_lora_fwd_grouped(a["x"], a["M"], a["K"], a["G"], a["pk"], a["q"], a["st"], a["n"],
+                                            a["A"], a["B"], a["r"], 0.0, a["y"], a["ws"], a["wsb"], V(0))
+    assert call(G=0) == 2 and call(G=9) == 2 and call(K=96) == 2 and call(n=N(64, 0)) == 2
+    assert call(x=V(0)) == 1 and call(pk=P(f, 0)) == 1 and call(y=P(f, 0)) == 1 and call(r=8) == 1
+    assert call(y=P(f, o)) == 3 and call(pk=P(o, f)) == 3 and call(r=129, A=P(f, f), B=P(f, f)) == 4
+    assert call(r=8, A=P(f, f), B=P(f, f)) == 5      # workspace needed for the adapters' t
+
+
 def test_quantize_dq_dequant_reject_bad_arguments():
     L = _lib.lib()
     assert L.qlora_nf4_quantize(V(0), 0, 64, FAKE, FAKE, V(0)) == 1

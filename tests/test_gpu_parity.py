@@ -685,3 +685,34 @@ def test_format_error_ordering_on_7b_weight(qops):
     print({f"{['nf4', 'int4', 'fp4'][f]}{'' if dq else '_nodq'}": round(e, 5) for (f, dq), e in err.items()})
     for dq in (True, False):
         assert err[0, dq] < err[1, dq] and err[0, dq] < err[2, dq]
+
+
+# ---------------------------------------------------------------------------
+# grouped forward of weights that share x
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,r", [(1, 16), (5, 0), (16, 16), (40, 16)])
+def test_grouped_forward_equals_single_calls(qops, M, r):
+    K, Ns = 512, [512, 200, 64]
+    x = dev(synth.activations(M, K, 950))
+    qws, As, Bs = [], [], []
+    for i, N in enumerate(Ns):
+        qws.append(gpu_quant(qops, synth.weight(N, K, 960 + i)))
+        A, B = synth.adapters(N, K, max(r, 1), 970 + i, 980 + i)
+        As.append(dev(A) if r else None)
+        Bs.append(dev(B) if r else None)
+    outs = qops.lora_fwd_grouped(x, qws, As if r else None, Bs if r else None, 32.0)
+    for i in range(3):
+        one = qops.lora_fwd(x, qws[i], As[i], Bs[i], 32.0)
+        assert torch.equal(outs[i].view(torch.int16), one.view(torch.int16)), i
+
+
+def test_grouped_forward_7b_qkv(qops):
+    c = synth.CONFIGS["7b_attn"]
+    N, K, r, alpha = c["N"], c["K"], c["r"], c["alpha"]
+    x = dev(synth.activations(16, K, 990))
+    qws = [gpu_quant(qops, synth.weight(N, K, 991 + i)) for i in range(3)]
+    ad = [synth.adapters(N, K, r, 995 + i, 998 + i) for i in range(3)]
+    As, Bs = [dev(a) for a, _ in ad], [dev(b) for _, b in ad]
+    outs = qops.lora_fwd_grouped(x, qws, As, Bs, alpha)
+    for i in range(3):
+        assert torch.equal(outs[i].view(torch.int16), qops.lora_fwd(x, qws[i], As[i], Bs[i], alpha).view(torch.int16))
