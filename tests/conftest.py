@@ -13,11 +13,6 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long CPU test")
 
 
-def pytest_collection_modifyitems(config, items):
-    # GPU tests run in one process on the GPU machine; nothing to reorder here.
-    pass
-
-
 @pytest.fixture(scope="session")
 def repo_root():
     return ROOT
