@@ -1,28 +1,28 @@
 #!/usr/bin/env python3
 """Benchmark of the NF4 dequant-GEMM hot path on one MI355X.
 
-Default workload: the 7B-shaped attention projection W [4096, 4096] with
-NF4 + double quantization, LoRA r=16 (alpha 32), decode shapes. One step is
-one pass of the whole hot path over one batch of synthetic input:
-  quantize W (fp32 -> NF4 codes + block absmax) and double-quantize the
-  constants (one fused kernel)
-  -> fused dequant forward at M = 1, 4 and 16 (each: LoRA down-projection +
-     dequant-GEMV with the LoRA epilogue)
-  -> fused dequant backward dX at M = 16.
-The dequantization itself happens inside the fused kernels. Weight copies are
-rotated (more of them than the 256 MB last-level cache holds) so the fused
-kernels stream their NF4 weights from HBM: each step quantizes copy c and runs
-the matmuls on copy c + C/2, which was written long before.
+Default workload: the whole 7B-shaped frozen stack, 32 layers x {q, k, v, o
+4096x4096; gate, up 11008x4096; down 4096x11008}, every linear stored as NF4
+with double-quantized constants and resident in HBM (3.34 GB), LoRA r=16
+(alpha 32) on all 224 linears. One step = 224 fused dequant forwards at
+M = 4096 tokens in layer order, then 224 fused dequant backward dX in reverse
+order; value = the step's algorithmic TFLOP/s (2MNK + 2Mr(K+N) per call).
 
-value = algorithmic bytes of the step / step time (GB/s); the algorithmic
-bytes are what the method must read and write once: fp32 W read + stored
-format (0.515869 bytes/param) written for the quantize, and per matmul the stored weight
-(0.515869 bytes/param), the adapters and the activations in and out.
+Beside the step, in the same run:
+  decode   the resident stack walked at decode shapes (M = 1, 4, 16 tokens):
+           per layer the fused forward of q, k, v (one grouped call: they
+           share x), o, gate and up (one grouped call), down -- every weight
+           byte streamed from HBM once per walk (3.34 GB, far beyond the
+           256 MB last-level cache); weight-stream GB/s per M, and the fused
+           backward dX walk at M = 16.
+  quantize the fp32 -> NF4 + double-quant kernel over all 224 weights, timed
+           as the stack is loaded (GB/s of fp32 read + stored format written).
+  context  a plain bf16 GEMM (torch.matmul on the dequantized weight) at each
+           training shape, a plain streaming read of the resident stack, and
+           the per-call times of every linear type.
 
-Other shapes (--config 7b_mlp_up, 65b_up, ...) run the MFMA-bound training
-path (forward + backward dX at M = 4096 / 2048) and report TFLOP/s;
---config 7b_stack runs the whole 7B-shaped stack resident in HBM (224 fused
-forwards, then 224 fused backward dX, at M = 4096) and reports TFLOP/s.
+Other workloads (--config 7b_attn, 7b_mlp_up, 65b_up, ...) time one weight:
+decode configs report GB/s, training configs TFLOP/s.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 """
@@ -45,9 +45,9 @@ NF4_BYTES_PER_PARAM = 0.5 + 1 / 64 + 4 / 16384
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--config", default="7b_attn",
+    p.add_argument("--config", default="7b_stack",
                    help="tiny, 7b_attn, 7b_mlp_up, 7b_mlp_down, 65b_up, 65b_attn or 7b_stack")
     p.add_argument("--copies", type=int, default=0, help="weight copies rotated (0 = auto)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -100,6 +100,10 @@ class Workload:
             # enough fp32 + NF4 copies to exceed the 256 MB last-level cache twice
             copies = int(min(64, max(4, np.ceil(2 * 256e6 / (nbytes_w + N * K * NF4_BYTES_PER_PARAM)))))
             copies += copies % 2
+            if max(c["M"]) <= 16:
+                # decode calls read only the NF4 copy: 32 of them (>= 277 MB
+                # at 4096x4096) exceed the last-level cache on their own
+                copies = max(copies, 32)
         self.C = copies
         # distinct weights per copy (scaled by 1 + c/1024, same distribution shape)
         self.w = [w_t * (1.0 + i / 1024.0) for i in range(copies)]
@@ -209,10 +213,11 @@ class StackWorkload:
     backward dX in reverse order. Each linear has its own synthetic x and dY
     (no attention, norms or activation functions between the linears); outputs
     of equal shape share a buffer. W, adapters and activations are drawn on the
-    device from the per-linear seeds, W is quantized once before timing and its
-    fp32 copy freed."""
+    device from the per-linear seeds, W is quantized once before timing (those
+    quantize launches are timed) and its fp32 copy freed."""
 
     name = "7b_stack"
+    DECODE_M = (1, 4, 16)
 
     def __init__(self):
         import torch
@@ -223,18 +228,53 @@ class StackWorkload:
         self.M, self.r, self.alpha = synth.STACK_M, synth.STACK_R, synth.STACK_ALPHA
         self.Ms, self.bwd_M, self.decode, self.C = [self.M], [self.M], False, 1
         self.lay = []
+        qstream = torch.cuda.Stream()
+        qev = []
         for l in range(self.L):
             row = []
             for j in range(len(self.lin)):
                 d = synth.stack_linear_device(l, j, self.M)
-                d["qw"] = ops.quantize_weight(d.pop("w"))
+                w = d.pop("w")
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                with torch.cuda.stream(qstream):
+                    e0.record(qstream)
+                    d["qw"] = ops.quantize_weight(w)
+                    e1.record(qstream)
+                qev.append((e0, e1, w.numel()))
+                torch.cuda.synchronize()
+                del w
                 row.append(d)
             self.lay.append(row)
+        torch.cuda.synchronize()
+        qms = sum(e0.elapsed_time(e1) for e0, e1, _ in qev)
+        qbytes = sum(quantize_bytes(n, 1) for _, _, n in qev)
+        self.quantize = {"ms_total": round(qms, 4), "weights": len(qev), "GB/s": round(qbytes / qms / 1e6, 1),
+                         "hbm_frac": round(qbytes / qms / 1e6 / HBM_PEAK_GBS, 4), "algorithmic_bytes": qbytes,
+                         "kernel": "k_quantize",
+                         "note": "fp32 W read once + NF4 codes, absmax, int8 scales and steps written once, "
+                                 "summed over the 224 quantize launches as the stack is loaded (each weight "
+                                 "freshly drawn, 64-180 MB of fp32)"}
         self.nf4_bytes = sum(d["qw"].nbytes for row in self.lay for d in row)
         self.y = {N: torch.empty((self.M, N), dtype=torch.bfloat16, device="cuda") for _, N, _ in self.lin}
         self.dx = {K: torch.empty((self.M, K), dtype=torch.bfloat16, device="cuda") for _, _, K in self.lin}
         self.ws = ops.Workspace("cuda")
-        self.ws.get(max(ops.workspace_bytes(op, self.M, N, K, self.r) for op in (0, 1) for _, N, K in self.lin))
+        need = max(ops.workspace_bytes(op, M, N, K, self.r) for op in (0, 1) for _, N, K in self.lin
+                   for M in (self.M,) + self.DECODE_M)
+        self.ws.get(max(need, 3 * max(ops.workspace_bytes(0, M, N, K, self.r) for _, N, K in self.lin
+                                      for M in self.DECODE_M)))
+        # decode inputs: one x per contraction size and M (the weights differ,
+        # which is what streams), outputs per (M, N)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(7)
+        self.xd = {(M, K): torch.randn((M, K), generator=g, device="cuda").bfloat16()
+                   for M in self.DECODE_M for K in (4096, 11008)}
+        self.dyd = {(M, N): torch.randn((M, N), generator=g, device="cuda").bfloat16()
+                    for M in self.DECODE_M for N in (4096, 11008)}
+        self.yd = {(M, N): torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+                   for M in self.DECODE_M for N in (4096, 11008)}
+        self.dxd = {(M, K): torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+                    for M in self.DECODE_M for K in (4096, 11008)}
         torch.cuda.synchronize()
 
     def _fwd(self, l, j):
@@ -258,6 +298,9 @@ class StackWorkload:
         return ([(f"fwd_{self.lin[j][0]}", [self._fwd(l, j) for l in range(self.L)]) for j in range(nl)] +
                 [(f"bwd_{self.lin[j][0]}", [self._bwd(l, j) for l in range(self.L)]) for j in range(nl)])
 
+    def calls_per_step(self, label):
+        return self.L
+
     def work(self):
         wk = {}
         for name, N, K in self.lin:
@@ -268,6 +311,42 @@ class StackWorkload:
     def step_work(self):
         wk = self.work()
         return (self.L * sum(b for b, _ in wk.values()), self.L * sum(f for _, f in wk.values()))
+
+    # -- decode walks over the resident stack ------------------------------
+    def decode_walk(self, M):
+        """The fused forwards of one decode pass at M tokens, in layer order:
+        per layer q/k/v as one grouped call (shared x), o, gate/up as one
+        grouped call, down."""
+        ops, a, ws = self.ops, self.alpha, self.ws
+        x4, x11 = self.xd[(M, 4096)], self.xd[(M, 11008)]
+        fns = []
+        for l in range(self.L):
+            q, k, v, o, gt, up, dn = self.lay[l]
+            fns.append(lambda q=q, k=k, v=v: ops.lora_fwd_grouped(
+                x4, [q["qw"], k["qw"], v["qw"]], [q["A"], k["A"], v["A"]], [q["B"], k["B"], v["B"]], a, ws=ws))
+            fns.append(lambda o=o: ops.lora_fwd(x4, o["qw"], o["A"], o["B"], a, out=self.yd[(M, 4096)], ws=ws))
+            fns.append(lambda gt=gt, up=up: ops.lora_fwd_grouped(
+                x4, [gt["qw"], up["qw"]], [gt["A"], up["A"]], [gt["B"], up["B"]], a, ws=ws))
+            fns.append(lambda dn=dn: ops.lora_fwd(x11, dn["qw"], dn["A"], dn["B"], a, out=self.yd[(M, 4096)],
+                                                  ws=ws))
+        return fns
+
+    def decode_bwd_walk(self, M):
+        """The fused backward dX of every linear at M tokens, layers in reverse."""
+        ops, a, ws = self.ops, self.alpha, self.ws
+        fns = []
+        for l in reversed(range(self.L)):
+            for j in reversed(range(len(self.lin))):
+                _, N, K = self.lin[j]
+                d = self.lay[l][j]
+                fns.append(lambda d=d, N=N, K=K: ops.bwd_dx(self.dyd[(M, N)], d["qw"], d["A"], d["B"], a,
+                                                            out=self.dxd[(M, K)], ws=ws))
+        return fns
+
+    def walk_bytes(self, M):
+        """Algorithmic bytes of one walk: every weight's stored format and
+        adapters once, plus each call's activations in and out."""
+        return sum(matmul_bytes(M, N, K, self.r, 0) for _, N, K in self.lin) * self.L
 
     def describe(self):
         return (f"7B-shaped frozen stack: {self.L} layers x {{q,k,v,o 4096x4096; gate,up 11008x4096; "
@@ -281,6 +360,32 @@ class StackWorkload:
 
     def config_extra(self):
         return {"layers": self.L, "linears": [list(t) for t in self.lin], "nf4_resident_bytes": self.nf4_bytes}
+
+
+def graph_of(fns, stream):
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for fn in fns:
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, stream, reps):
+    """ms per replay of a captured graph, from events on its stream."""
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 
 def run_gpu(args):
@@ -320,6 +425,8 @@ def run_gpu(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(end) / args.steps
+    print(f"# step: {ms_step:.4f} ms ({args.steps} steps, {wall:.2f} s wall)", file=sys.stderr, flush=True)
+    del graphs
 
     # per-call durations: for each call, one graph runs its launches back to
     # back (single matrix: once per weight copy of the rotation; stack: that
@@ -330,21 +437,9 @@ def run_gpu(args):
     groups = [(lab, fns, None) for lab, fns in wl.timing_groups()] + wl.extra_groups()
     for lab, fns, work in groups:
         reps = max(2, args.steps // len(fns))
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for fn in fns:
-                fn()
-        g.replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            e0.record(stream)
-            for _ in range(reps):
-                g.replay()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / (reps * len(fns))
+        g = graph_of(fns, stream)
+        ms = time_graph(g, stream, reps) / len(fns)
+        del g
         if work is None:
             per_call[lab] = ms
         else:
@@ -352,12 +447,72 @@ def run_gpu(args):
                           "hbm_frac": round(work[0] / ms / 1e6 / HBM_PEAK_GBS, 4),
                           "TFLOP/s": round(work[1] / ms / 1e9, 2)}
     wl.extra = extra
+    wl.decode_result = decode_walks(wl, stream) if isinstance(wl, StackWorkload) else None
     return wl, ms_step, per_call, wall
 
 
-# ---------------------------------------------------------------------------
-# CPU baseline: the oracle, timed on the host on a bounded sample
-# ---------------------------------------------------------------------------
+def decode_walks(wl, stream, reps=10):
+    """Weight-stream rate of the decode walks over the resident stack."""
+    out = {}
+    for M in wl.DECODE_M:
+        g = graph_of(wl.decode_walk(M), stream)
+        ms = time_graph(g, stream, reps)
+        del g
+        b = wl.walk_bytes(M)
+        out[f"fwd_M{M}"] = {"ms": round(ms, 4), "GB/s": round(b / ms / 1e6, 1),
+                            "hbm_frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4), "bytes": b,
+                            "launch_groups": 4 * wl.L}
+        print(f"# decode walk M={M}: {ms:.4f} ms, {b / ms / 1e6:.1f} GB/s", file=sys.stderr, flush=True)
+    M = 16
+    g = graph_of(wl.decode_bwd_walk(M), stream)
+    ms = time_graph(g, stream, reps)
+    del g
+    b = wl.walk_bytes(M)
+    out[f"bwd_M{M}"] = {"ms": round(ms, 4), "GB/s": round(b / ms / 1e6, 1),
+                        "hbm_frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4), "bytes": b,
+                        "launch_groups": len(wl.lin) * wl.L}
+    print(f"# decode bwd walk M={M}: {ms:.4f} ms", file=sys.stderr, flush=True)
+    return out
+
+
+def context_figures(wl, stream):
+    """Plain ROCm-library and streaming figures beside the fused kernels:
+    torch.matmul (hipBLASLt) in bf16 on the dequantized weight at each
+    training shape, and a streaming read of the resident NF4 stack."""
+    import torch
+    ops = wl.ops
+    out = {"bf16_gemm_on_dequantized_weight": {}}
+    seen = {}
+    for j, (name, N, K) in enumerate(wl.lin):
+        if (N, K) in seen:
+            continue
+        seen[(N, K)] = name
+        d = wl.lay[0][j]
+        wdq = ops.dequant(d["qw"])
+        x, dy = d["x"], d["dy"]
+        yb = torch.empty((wl.M, N), dtype=torch.bfloat16, device="cuda")
+        db = torch.empty((wl.M, K), dtype=torch.bfloat16, device="cuda")
+        f = 2 * wl.M * N * K
+        gf = graph_of([lambda: torch.matmul(x, wdq.t(), out=yb)], stream)
+        gb = graph_of([lambda: torch.matmul(dy, wdq, out=db)], stream)
+        mf, mb = time_graph(gf, stream, 10), time_graph(gb, stream, 10)
+        out["bf16_gemm_on_dequantized_weight"][f"{name} {N}x{K}"] = {
+            "fwd_ms": round(mf, 4), "fwd_TFLOP/s": round(f / mf / 1e9, 1),
+            "bwd_ms": round(mb, 4), "bwd_TFLOP/s": round(f / mb / 1e9, 1)}
+        del gf, gb, wdq, yb, db
+    # streaming read: one float sum over every resident weight's packed codes
+    packs = [d["qw"].packed for row in wl.lay for d in row]
+    tot = torch.zeros((), dtype=torch.float32, device="cuda")
+    views = [p.view(torch.float32) for p in packs]
+    g = graph_of([lambda: [tot.add_(v.sum()) for v in views]], stream)
+    ms = time_graph(g, stream, 5)
+    b = sum(p.numel() for p in packs)
+    out["stream_read_packed_stack"] = {"ms": round(ms, 4), "GB/s": round(b / ms / 1e6, 1), "bytes": b,
+                                       "how": "torch sum over each of the 224 packed code buffers, one graph"}
+    del g
+    return out
+
+
 def cpu_baseline(args, wl):
     import synth
     from oracle import gemm, nf4
@@ -466,6 +621,7 @@ CALL_KERNEL = {"quantize_dq": ("k_quantize", "quant.hip"), "fwd": ("k_gemv_fwd",
 
 
 def kernel_of(label, M):
+    """(kernel, source) that does the arithmetic of a call label."""
     key = label if label == "quantize_dq" else label.split("_")[0]
     if key in ("fwd", "bwd") and M > 16:
         key += "_big"
@@ -541,20 +697,28 @@ def main():
                         "hbm_frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4)}
         if f:
             kernels[lab]["TFLOP/s"] = round(f / ms / 1e9, 2)
-    dom = max(per_call, key=per_call.get)
-    b, f = wk[dom]
-    kname, unit_src = kernel_of(dom, max(wl.Ms))
+    # the roofline kernel: the one with the largest share of the step's time
+    # (per-call time x calls per step, summed over the calls that run it)
+    share = {}
+    for lab, ms in per_call.items():
+        kn = kernel_of(lab, max(wl.Ms))
+        n = wl.calls_per_step(lab) if hasattr(wl, "calls_per_step") else 1
+        t, b_, f_, labs = share.get(kn, (0.0, 0.0, 0.0, []))
+        share[kn] = (t + n * ms, b_ + n * wk[lab][0], f_ + n * wk[lab][1], labs + [lab])
+    (kname, unit_src), (t_k, b_k, f_k, labs_k) = max(share.items(), key=lambda kv: kv[1][0])
     traffic = read_traffic(kname, unit_src, wl.name)
-    if wl.decode or dom == "quantize_dq":
-        ach = b / per_call[dom] / 1e6
+    n_launch = sum(wl.calls_per_step(l) if hasattr(wl, "calls_per_step") else 1 for l in labs_k)
+    common = {"traffic": traffic, "kernel": kname, "calls": labs_k, "launches_per_step": n_launch,
+              "ms_per_launch": round(t_k / n_launch, 5), "step_time_share": round(t_k / ms_step, 4)}
+    if wl.decode or kname == "k_quantize":
+        ach = b_k / t_k / 1e6
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kname, "call": dom,
-                "algorithmic_bytes": b, "ms": round(per_call[dom], 5)}
+                "frac": round(ach / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": b_k / n_launch}
     else:
-        ach = f / per_call[dom] / 1e9
+        ach = f_k / t_k / 1e9
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                "frac": round(ach / MFMA_BF16_PEAK_TFS, 4), "traffic": traffic, "kernel": kname, "call": dom,
-                "algorithmic_flops": f, "ms": round(per_call[dom], 5)}
+                "frac": round(ach / MFMA_BF16_PEAK_TFS, 4), "algorithmic_flops_per_launch": f_k / n_launch}
+    roof.update(common)
     metric = "fused NF4-dequant GEMM TFLOP/s + weight-stream GB/s (% of MI355X roofline)"
     if wl.decode:
         value, unit = step_bytes / ms_step / 1e6, "GB/s"
@@ -572,6 +736,21 @@ def main():
         "kernels": kernels,
         "step_bytes": step_bytes, "step_flops": step_flops,
     }
+    if getattr(wl, "decode_result", None):
+        dec = wl.decode_result
+        fw = [v for k, v in dec.items() if k.startswith("fwd")]
+        tb, tm = sum(v["bytes"] for v in fw), sum(v["ms"] for v in fw)
+        ach = tb / tm / 1e6
+        line["decode"] = dict(dec, note="the resident stack walked at M tokens: per layer q/k/v (one grouped "
+                                        "call), o, gate/up (one grouped call), down; bytes = every weight's "
+                                        "stored format + adapters + activations once; bwd = backward dX of "
+                                        "all 224 linears at M = 16")
+        line["roofline_decode"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": round(ach / HBM_PEAK_GBS, 4), "kernel": "k_gemv_fwd",
+                                   "traffic": read_traffic("k_gemv_fwd", "small.hip", "7b_stack_decode"),
+                                   "over": "fwd walks at M = " + ", ".join(str(m) for m in wl.DECODE_M)}
+        line["quantize"] = wl.quantize
+        line["context"] = context_figures(wl, torch.cuda.Stream())
     if wl.extra:
         line["outside_step"] = dict(wl.extra, note="timed alone at the step's shapes: decode, one grouped "
                                                    "forward of three weights sharing x (qlora_nf4_lora_fwd_"

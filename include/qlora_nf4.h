@@ -91,7 +91,7 @@ int qlora_nf4_quantize(const void* w, int wdt, int64_t numel, uint8_t* packed,
  * Double quantization of the block constants to int8 in groups of 256
  * (figure 4 of "A 65B fine-tune on the GPU you already have").
  *   absmax   [nblocks] fp32 >= 0 (from qlora_nf4_quantize).
- *   nblocks  > 0.
+ *   nblocks  in 1 .. 2^31 - 1.
  *   qscale   [nblocks] int8 out: rne(fp32(absmax / d)), clamped to [-127, 127].
  *   step     [ceil(nblocks/256)] fp32 out: d = fp32(group max / 127); a group
  *            whose max is 0 has d = 0 and all q = 0. The last group may be
@@ -146,8 +146,11 @@ size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r);
  *           qlora_workspace_bytes(0, M, N, K, r) bytes, 16-byte aligned
  *           (may be NULL when that is 0). Its contents are overwritten.
  * Products are bf16 x bf16 accumulated in fp32. x, packed, y, A, B and the
- * workspace must be 16-byte aligned. Size limits (here and in the two calls
- * below): M <= 2^31, N and K <= 2^24.
+ * workspace must be 16-byte aligned. Size limits (here and in every other
+ * matmul call: grouped forward, backward, merge, adapter gradients):
+ * M <= 2^31, N and K <= 2^21 (each operand is addressed through 32-bit
+ * buffer descriptors), and ceil(M/256) * ceil(max(N, K)/256) < 2^31 (the
+ * number of 256 x 256 output tiles); larger sizes return QLORA_ERR_SHAPE.
  */
 int qlora_nf4_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K,
                        const uint8_t* packed, const int8_t* qscale,
@@ -216,6 +219,7 @@ int qlora_nf4_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K,
  *           = 0 overwrites them, 1 adds the gradients to what they hold
  *           (accumulation over micro-batches).
  *   workspace / ws_bytes  at least qlora_workspace_bytes(2, M, N, K, r).
+ * Size limits as in qlora_nf4_lora_fwd, and M * max(N, K) <= 2^30.
  * Products are bf16 x bf16 accumulated in fp32; the result does not depend
  * on scheduling (partial sums are added in a fixed order). Every pointer must
  * be 16-byte aligned. The weight itself is not an argument: neither gradient

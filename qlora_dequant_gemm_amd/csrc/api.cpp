@@ -37,6 +37,22 @@ int check_adapter(const uint16_t* A, const uint16_t* B, int r) {
   return QLORA_OK;
 }
 
+// Sizes of the matmul entry points. The kernels address each operand through
+// 32-bit buffer descriptors whose byte range is at most 512 rows x max(N, K)
+// x 2 bytes (or r x max(N, K) x 2 with r <= 128), so N and K are capped at
+// 2^21; the tiled kernels number their 256 x 256 output tiles with 32-bit
+// integers.
+constexpr int64_t kMaxDim = int64_t{1} << 21;
+constexpr int64_t kMaxM = int64_t{1} << 31;
+
+int check_mm(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 64 || K % QLORA_BLOCK != 0) return QLORA_ERR_SHAPE;
+  if (M > kMaxM || N > kMaxDim || K > kMaxDim) return QLORA_ERR_SHAPE;
+  const int64_t big = N > K ? N : K;
+  if (((M + 255) / 256) * ((big + 255) / 256) >= (int64_t{1} << 31)) return QLORA_ERR_SHAPE;
+  return QLORA_OK;
+}
+
 int check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (need == 0) return QLORA_OK;
   if (!ws || ws_bytes < need) return QLORA_ERR_WORKSPACE;
@@ -105,7 +121,7 @@ int qlora_nf4_quantize_dq(const void* w, int wdt, int64_t numel, uint8_t* packed
 
 int qlora_dq_scales(const float* absmax, int64_t nblocks, int8_t* qscale, float* step, void* stream) {
   if (!absmax || !qscale || !step) return QLORA_ERR_NULL;
-  if (nblocks <= 0 || nblocks > (int64_t{1} << 39)) return QLORA_ERR_SHAPE;
+  if (nblocks <= 0 || nblocks >= (int64_t{1} << 31)) return QLORA_ERR_SHAPE;
   return hip_status(qnf4::launch_dq_scales(absmax, nblocks, qscale, step, as_stream(stream)));
 }
 
@@ -127,8 +143,8 @@ int qlora_nf4_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K, const
   if (!x || !y) return QLORA_ERR_NULL;
   int st = check_weight(packed, qscale, step);
   if (st) return st;
-  if (M < 1 || N < 1 || K < 64 || K % QLORA_BLOCK != 0) return QLORA_ERR_SHAPE;
-  if (M > (int64_t{1} << 31) || N > (int64_t{1} << 24) || K > (int64_t{1} << 24)) return QLORA_ERR_SHAPE;
+  st = check_mm(M, N, K);
+  if (st) return st;
   st = check_adapter(A, B, r);
   if (st) return st;
   if (!aligned16(x) || !aligned16(y)) return QLORA_ERR_ALIGN;
@@ -146,8 +162,7 @@ int qlora_nf4_lora_fwd_grouped(const uint16_t* x, int64_t M, int64_t K, int G, c
                                uint16_t* const* y, void* workspace, size_t ws_bytes, void* stream) {
   if (!x || !packed || !qscale || !step || !N || !y) return QLORA_ERR_NULL;
   if (G < 1 || G > qnf4::kMaxGroups) return QLORA_ERR_SHAPE;
-  if (M < 1 || K < 64 || K % QLORA_BLOCK != 0 || M > (int64_t{1} << 31) || K > (int64_t{1} << 24))
-    return QLORA_ERR_SHAPE;
+  if (check_mm(M, 1, K)) return QLORA_ERR_SHAPE;
   if (r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_RANK;
   if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
   if (!aligned16(x)) return QLORA_ERR_ALIGN;
@@ -156,7 +171,7 @@ int qlora_nf4_lora_fwd_grouped(const uint16_t* x, int64_t M, int64_t K, int G, c
     int st = check_weight(packed[i], qscale[i], step[i]);
     if (st) return st;
     if (!y[i]) return QLORA_ERR_NULL;
-    if (N[i] < 1 || N[i] > (int64_t{1} << 24)) return QLORA_ERR_SHAPE;
+    if (check_mm(M, N[i], K)) return QLORA_ERR_SHAPE;
     if (!aligned16(y[i])) return QLORA_ERR_ALIGN;
     st = check_adapter(r ? A[i] : nullptr, r ? B[i] : nullptr, r);
     if (st) return st;
@@ -177,8 +192,9 @@ int qlora_nf4_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K, const 
   if (!dy || !dx) return QLORA_ERR_NULL;
   int st = check_weight(packed, qscale, step);
   if (st) return st;
-  if (M < 1 || N < 1 || N % 8 != 0 || K < 64 || K % QLORA_BLOCK != 0) return QLORA_ERR_SHAPE;
-  if (M > (int64_t{1} << 31) || N > (int64_t{1} << 24) || K > (int64_t{1} << 24)) return QLORA_ERR_SHAPE;
+  if (N % 8 != 0) return QLORA_ERR_SHAPE;
+  st = check_mm(M, N, K);
+  if (st) return st;
   st = check_adapter(A, B, r);
   if (st) return st;
   if (!aligned16(dy) || !aligned16(dx)) return QLORA_ERR_ALIGN;
@@ -231,8 +247,7 @@ int qlora_nf4_merge(const uint8_t* packed, const int8_t* qscale, const float* st
   int st = check_weight(packed, qscale, step);
   if (st) return st;
   if (!out) return QLORA_ERR_NULL;
-  if (N < 1 || K < 64 || K % QLORA_BLOCK != 0 || N > (int64_t{1} << 24) || K > (int64_t{1} << 24))
-    return QLORA_ERR_SHAPE;
+  if (check_mm(1, N, K)) return QLORA_ERR_SHAPE;
   st = check_adapter(A, B, r);
   if (st) return st;
   if (!aligned16(out)) return QLORA_ERR_ALIGN;
@@ -245,8 +260,9 @@ int qlora_lora_grad(const uint16_t* x, const uint16_t* dy, int64_t M, int64_t N,
                     const uint16_t* B, int r, float alpha, float* dA, float* dB, int accumulate, void* workspace,
                     size_t ws_bytes, void* stream) {
   if (!x || !dy || !dA || !dB) return QLORA_ERR_NULL;
-  if (M < 1 || N < 1 || N % 8 != 0 || K < 64 || K % QLORA_BLOCK != 0) return QLORA_ERR_SHAPE;
-  if (M > (int64_t{1} << 31) || N > (int64_t{1} << 24) || K > (int64_t{1} << 24)) return QLORA_ERR_SHAPE;
+  if (N % 8 != 0 || check_mm(M, N, K)) return QLORA_ERR_SHAPE;
+  // one row split of x or dY is addressed by one 32-bit descriptor
+  if (M * (N > K ? N : K) > (int64_t{1} << 30)) return QLORA_ERR_SHAPE;
   if (r < 1 || r > QLORA_MAX_RANK) return QLORA_ERR_RANK;
   if (!A || !B) return QLORA_ERR_NULL;
   if (accumulate != 0 && accumulate != 1) return QLORA_ERR_SHAPE;

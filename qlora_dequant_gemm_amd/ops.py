@@ -22,11 +22,20 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _need(t, dtype, name):
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
+def _need(t, dtype, name, device=None, shape=None):
+    """Checks, in this order: a tensor, of `dtype`, of `shape` (when given),
+    on the GPU (on `device` when given), contiguous. Shapes are checked before
+    the device, so that mismatches are caught from metadata alone."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 
@@ -36,7 +45,21 @@ class NF4Weight:
 
     def __init__(self, packed, qscale, step, shape):
         self.packed, self.qscale, self.step = packed, qscale, step
-        self.shape = tuple(shape)
+        self.shape = tuple(int(d) for d in shape)
+        if len(self.shape) != 2:
+            raise ValueError("an NF4 weight is two-dimensional [N, K]")
+        N, K = self.shape
+        nb = N * K // BLOCK
+        if N < 1 or K < BLOCK or K % BLOCK:
+            raise ValueError(f"an NF4 weight needs N >= 1 and K a multiple of {BLOCK}, got [{N}, {K}]")
+        parts = [(packed, torch.uint8, N * K // 2, "packed"), (qscale, torch.int8, nb, "qscale"),
+                 (step, torch.float32, (nb + DQ_GROUP - 1) // DQ_GROUP, "step")]
+        for t, dt, n, name in parts:
+            _shape(t, (n,), name)
+            if t.dtype != dt:
+                raise ValueError(f"{name} must be {dt}, got {t.dtype}")
+        for t, dt, n, name in parts:
+            _need(t, dt, name, packed.device, shape=(n,))
 
     @property
     def nbytes(self):
@@ -112,9 +135,7 @@ def quantize_weight(w):
 def dequant(qw, out=None):
     numel = qw.packed.numel() * 2
     dev = qw.packed.device
-    if out is None:
-        out = torch.empty(qw.shape, dtype=torch.bfloat16, device=dev)
-    _need(out, torch.bfloat16, "out")
+    out = _check_out(out, qw.shape, dev, "out")
     _lib.check("qlora_nf4_dequant", _lib.lib().qlora_nf4_dequant(
         _ptr(qw.packed), _ptr(qw.qscale), _ptr(qw.step), numel, _ptr(out), _stream(dev)))
     return out
@@ -139,17 +160,64 @@ class Workspace:
         return self.buf
 
 
+def _shape(t, shape, name):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _rows(t, name):
+    if not isinstance(t, torch.Tensor) or t.dim() != 2:
+        raise ValueError(f"{name} must be a two-dimensional tensor")
+    return t.shape[0]
+
+
+def _adapter_rank(A, B, N, K):
+    """Rank of the adapter pair A [r, K], B [N, r] (0 for none); shapes only."""
+    if (A is None) != (B is None):
+        raise ValueError("A and B must both be given or both be None")
+    if A is None:
+        return 0
+    r = _rows(A, "A")
+    _shape(A, (r, K), "A")
+    _shape(B, (N, r), "B")
+    return r
+
+
+def _check_adapters(A, B, N, K, dev):
+    """Rank of the adapter pair A [r, K], B [N, r] (0 for none), checked."""
+    r = _adapter_rank(A, B, N, K)
+    if r:
+        _need(A, torch.bfloat16, "A", dev, shape=(r, K))
+        _need(B, torch.bfloat16, "B", dev, shape=(N, r))
+    return r
+
+
+def _check_out(out, shape, dev, name):
+    if out is None:
+        return torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    _need(out, torch.bfloat16, name, dev, shape=shape)
+    return out
+
+
+def _check_weight(qw, dev):
+    if qw.packed.device != dev:
+        raise ValueError("the stored weight must be on the input's device")
+
+
 def lora_fwd(x, qw, A=None, B=None, alpha=0.0, out=None, ws=None):
     """y = x . deq(W)^T + (alpha/r) . (x . A^T) . B^T, all bf16 [M, K] -> [M, N]."""
+    N, K = qw.shape
+    M = _rows(x, "x")
+    _shape(x, (M, K), "x")
+    _adapter_rank(A, B, N, K)
+    if out is not None:
+        _shape(out, (M, N), "out")
     _need(x, torch.bfloat16, "x")
-    M, K = x.shape
-    N = qw.shape[0]
-    r = 0 if A is None else A.shape[0]
-    if A is not None:
-        _need(A, torch.bfloat16, "A")
-        _need(B, torch.bfloat16, "B")
-    if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check_weight(qw, x.device)
+    r = _check_adapters(A, B, N, K, x.device)
+    out = _check_out(out, (M, N), x.device, "out")
     need = workspace_bytes(0, M, N, K, r)
     wsb = (ws or Workspace(x.device)).get(need)
     _lib.check("qlora_nf4_lora_fwd", _lib.lib().qlora_nf4_lora_fwd(
@@ -161,13 +229,31 @@ def lora_fwd(x, qw, A=None, B=None, alpha=0.0, out=None, ws=None):
 def lora_fwd_grouped(x, qws, As=None, Bs=None, alpha=0.0, outs=None, ws=None):
     """The forward of several weights sharing x (one launch for M <= 16):
     returns [x . deq(W_i)^T + (alpha/r) . (x . A_i^T) . B_i^T for each i]."""
-    _need(x, torch.bfloat16, "x")
-    M, K = x.shape
+    M = _rows(x, "x")
+    K = x.shape[1]
     G = len(qws)
-    r = 0 if As is None else As[0].shape[0]
+    if (As is None) != (Bs is None) or (As is not None and (len(As) != G or len(Bs) != G)):
+        raise ValueError("As and Bs must both be None or both hold one adapter per weight")
+    if outs is not None and len(outs) != G:
+        raise ValueError("one output per weight")
     Ns = [qw.shape[0] for qw in qws]
+    ranks = set()
+    for i, qw in enumerate(qws):
+        if qw.shape[1] != K:
+            raise ValueError(f"weight {i} is {qw.shape}, x has K = {K}")
+        ranks.add(_adapter_rank(As[i] if As is not None else None, Bs[i] if Bs is not None else None, Ns[i], K))
+        if outs is not None:
+            _shape(outs[i], (M, Ns[i]), f"outs[{i}]")
+    if len(ranks) != 1:
+        raise ValueError("every weight of a group must have adapters of one rank")
+    r = ranks.pop()
+    _need(x, torch.bfloat16, "x")
+    for i, qw in enumerate(qws):
+        _check_weight(qw, x.device)
+        _check_adapters(As[i] if As is not None else None, Bs[i] if Bs is not None else None, Ns[i], K, x.device)
     if outs is None:
         outs = [torch.empty((M, n), dtype=torch.bfloat16, device=x.device) for n in Ns]
+    outs = [_check_out(o, (M, n), x.device, f"outs[{i}]") for i, (o, n) in enumerate(zip(outs, Ns))]
     arr = lambda ts: (ctypes.c_void_p * G)(*[t.data_ptr() if t is not None else 0 for t in ts])
     need = G * workspace_bytes(0, M, max(Ns), K, r)
     wsb = (ws or Workspace(x.device)).get(need)
@@ -180,15 +266,16 @@ def lora_fwd_grouped(x, qws, As=None, Bs=None, alpha=0.0, outs=None, ws=None):
 
 def bwd_dx(dy, qw, A=None, B=None, alpha=0.0, out=None, ws=None):
     """dX = dY . deq(W) + (alpha/r) . (dY . B) . A, bf16 [M, N] -> [M, K]."""
+    N, K = qw.shape
+    M = _rows(dy, "dy")
+    _shape(dy, (M, N), "dy")
+    _adapter_rank(A, B, N, K)
+    if out is not None:
+        _shape(out, (M, K), "out")
     _need(dy, torch.bfloat16, "dy")
-    M, N = dy.shape
-    K = qw.shape[1]
-    r = 0 if A is None else A.shape[0]
-    if A is not None:
-        _need(A, torch.bfloat16, "A")
-        _need(B, torch.bfloat16, "B")
-    if out is None:
-        out = torch.empty((M, K), dtype=torch.bfloat16, device=dy.device)
+    _check_weight(qw, dy.device)
+    r = _check_adapters(A, B, N, K, dy.device)
+    out = _check_out(out, (M, K), dy.device, "out")
     need = workspace_bytes(1, M, N, K, r)
     wsb = (ws or Workspace(dy.device)).get(need)
     _lib.check("qlora_nf4_bwd_dx", _lib.lib().qlora_nf4_bwd_dx(
@@ -201,21 +288,25 @@ def lora_grad(x, dy, A, B, alpha, dA=None, dB=None, accumulate=False, ws=None):
     """Adapter gradients (dA [r, K], dB [N, r], fp32) of one QLoRA linear:
     dB = (alpha/r) . dY^T . bf16(x . A^T), dA = (alpha/r) . bf16(dY . B)^T . x.
     With accumulate=True they are added to dA and dB."""
+    M = _rows(x, "x")
+    _rows(dy, "dy")
+    K, N = x.shape[1], dy.shape[1]
+    r = _adapter_rank(A, B, N, K)
+    _shape(dy, (M, N), "dy")
+    if dA is not None:
+        _shape(dA, (r, K), "dA")
+    if dB is not None:
+        _shape(dB, (N, r), "dB")
     _need(x, torch.bfloat16, "x")
-    _need(dy, torch.bfloat16, "dy")
-    _need(A, torch.bfloat16, "A")
-    _need(B, torch.bfloat16, "B")
-    M, K = x.shape
-    N = dy.shape[1]
-    r = A.shape[0]
-    if dy.shape[0] != M or A.shape[1] != K or tuple(B.shape) != (N, r):
-        raise ValueError("inconsistent shapes")
+    _need(dy, torch.bfloat16, "dy", x.device, shape=(M, N))
+    _need(A, torch.bfloat16, "A", x.device, shape=(r, K))
+    _need(B, torch.bfloat16, "B", x.device, shape=(N, r))
     if dA is None:
         dA = (torch.zeros if accumulate else torch.empty)((r, K), dtype=torch.float32, device=x.device)
     if dB is None:
         dB = (torch.zeros if accumulate else torch.empty)((N, r), dtype=torch.float32, device=x.device)
-    _need(dA, torch.float32, "dA")
-    _need(dB, torch.float32, "dB")
+    _need(dA, torch.float32, "dA", x.device, shape=(r, K))
+    _need(dB, torch.float32, "dB", x.device, shape=(N, r))
     need = workspace_bytes(2, M, N, K, r)
     wsb = (ws or Workspace(x.device)).get(need)
     _lib.check("qlora_lora_grad", _lib.lib().qlora_lora_grad(
@@ -270,16 +361,12 @@ def merge(qw, A=None, B=None, alpha=0.0, out=None):
     """bf16 [N, K] = bf16(deq(W) + (alpha/r) . B . A): the adapter folded into one
     dense weight (exactly the dequantized weight when there is no adapter)."""
     N, K = qw.shape
-    r = 0 if A is None else A.shape[0]
-    if A is not None:
-        _need(A, torch.bfloat16, "A")
-        _need(B, torch.bfloat16, "B")
-        if tuple(A.shape) != (r, K) or tuple(B.shape) != (N, r):
-            raise ValueError("inconsistent adapter shapes")
     dev = qw.packed.device
-    if out is None:
-        out = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
-    _need(out, torch.bfloat16, "out")
+    _adapter_rank(A, B, N, K)
+    if out is not None:
+        _shape(out, (N, K), "out")
+    r = _check_adapters(A, B, N, K, dev)
+    out = _check_out(out, (N, K), dev, "out")
     _lib.check("qlora_nf4_merge", _lib.lib().qlora_nf4_merge(
         _ptr(qw.packed), _ptr(qw.qscale), _ptr(qw.step), N, K, _ptr(A), _ptr(B), r, float(alpha), _ptr(out),
         _stream(dev)))

@@ -217,3 +217,21 @@ def test_thresholds_sit_well_inside_quantize_cells():
     frac = pos - np.floor(pos)
     assert np.min(np.minimum(frac, 1 - frac)) / 64 > 1e-4
     assert len(set(np.floor(pos).astype(int))) == 15
+
+
+def test_size_limits_return_shape_errors():
+    """Sizes the kernels' 32-bit buffer descriptors or tile numbering cannot
+    address are rejected before anything is launched (N, K <= 2^21; the 256 x
+    256 tile count below 2^31; for the adapter gradients M * max(N, K) <= 2^30)."""
+    big = 1 << 21
+    assert _fwd(N=big + 64, K=64) == 2 and _fwd(K=big + 64) == 2
+    assert _fwd(M=(1 << 31) + 1) == 2
+    assert _fwd(M=1 << 31, N=big, K=64) == 2                    # 2^23 x 2^13 tiles
+    assert _bwd(N=big + 8, K=64, wsb=0, ws=V(0)) == 2 and _bwd(K=big + 64, wsb=0, ws=V(0)) == 2
+    assert _grad(M=1 << 20, N=2048, K=64) == 2                  # 2^31 > 2^30
+    assert _lib.lib().qlora_nf4_merge(FAKE, FAKE, FAKE, big + 1, 64, V(0), V(0), 0, 0.0, FAKE, V(0)) == 2
+    assert _lib.lib().qlora_dq_scales(FAKE, 1 << 31, FAKE, FAKE, V(0)) == 2
+    # the largest accepted sizes pass the shape checks (and stop at the
+    # workspace check, so nothing is launched)
+    assert _fwd(M=1 << 20, N=big, K=big, r=8, A=FAKE, B=FAKE) == 5
+    assert _grad(M=512, N=big, K=64, ws=V(0), wsb=0) == 5

@@ -716,3 +716,89 @@ def test_grouped_forward_7b_qkv(qops):
     outs = qops.lora_fwd_grouped(x, qws, As, Bs, alpha)
     for i in range(3):
         assert torch.equal(outs[i].view(torch.int16), qops.lora_fwd(x, qws[i], As[i], Bs[i], alpha).view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# decode shapes (M <= 16), every output against the fp64 oracle at full size.
+# Same element-wise bound as the tiled kernels, with ref, S and T taken from
+# the oracle's exact arithmetic (t = x . A^T and u = dY . B unrounded: the
+# kernels' bf16 rounding of them is within 2^-9 s.T, inside the bound).
+# The shapes cover every loop of the decode kernels: K = 4096 (the 7B
+# attention projection), K = 11008 (the 7B down projection: several K steps
+# per wave) and, for the backward, N = 11008 (the gate/up projections: several
+# weight-row steps per slice).
+# ---------------------------------------------------------------------------
+def _oracle_bound_ok(got, ref, S, T, scale):
+    bound = np.abs(ref) * 2.0 ** -8 + S * 2.0 ** -12 + T * (scale * 2.0 ** -8) + 1e-6
+    return int((np.abs(got - ref) > bound).sum())
+
+
+def _oracle_weight(w):
+    opk, oq, ostep, _ = nf4.quantize_all(w)
+    return nf4.dequantize(opk, oq, ostep).reshape(w.shape)
+
+
+DECODE_FWD = [("7b_attn", 1), ("7b_attn", 4), ("7b_attn", 16), ("7b_mlp_down", 1), ("7b_mlp_down", 16),
+              ("7b_mlp_up", 4)]
+
+
+@pytest.mark.parametrize("name,M", DECODE_FWD)
+def test_decode_forward_every_output_vs_oracle(qops, name, M):
+    inp = synth.config_inputs(name, M)
+    N, K, r, alpha = inp["N"], inp["K"], inp["r"], inp["alpha"]
+    qw = gpu_quant(qops, inp["w"])
+    got = to_f64(host_bits(qops.lora_fwd(dev(inp["x"]), qw, dev(inp["A"]), dev(inp["B"]), alpha)))
+    del qw
+    wd = _oracle_weight(inp["w"])
+    ref = gemm.lora_forward(inp["x"], wd, inp["A"], inp["B"], alpha, r)
+    x, W = to_f64(inp["x"]), to_f64(wd)
+    S = np.abs(x) @ np.abs(W).T
+    T = np.abs(x @ to_f64(inp["A"]).T) @ np.abs(to_f64(inp["B"])).T
+    assert _oracle_bound_ok(got, ref, S, T, alpha / r) == 0
+    assert rel_fro(got, ref) <= TIGHT
+
+
+DECODE_BWD = [("7b_attn", 16), ("7b_attn", 1), ("7b_mlp_up", 16), ("7b_mlp_up", 3), ("7b_mlp_down", 8)]
+
+
+@pytest.mark.parametrize("name,M", DECODE_BWD)
+def test_decode_backward_every_output_vs_oracle(qops, name, M):
+    inp = synth.config_inputs(name, M)
+    N, K, r, alpha = inp["N"], inp["K"], inp["r"], inp["alpha"]
+    qw = gpu_quant(qops, inp["w"])
+    got = to_f64(host_bits(qops.bwd_dx(dev(inp["dy"]), qw, dev(inp["A"]), dev(inp["B"]), alpha)))
+    del qw
+    wd = _oracle_weight(inp["w"])
+    ref = gemm.backward_dx(inp["dy"], wd, inp["A"], inp["B"], alpha, r)
+    dy, W = to_f64(inp["dy"]), to_f64(wd)
+    S = np.abs(dy) @ np.abs(W)
+    T = np.abs(dy @ to_f64(inp["B"])) @ np.abs(to_f64(inp["A"]))
+    assert _oracle_bound_ok(got, ref, S, T, alpha / r) == 0
+    assert rel_fro(got, ref) <= TIGHT
+
+
+@pytest.mark.parametrize("M,r,Ns,K", [(1, 16, [512, 200, 64], 512), (16, 16, [4096, 4096, 4096], 4096),
+                                      (4, 0, [11008, 11008], 4096), (40, 16, [300, 520], 320),
+                                      (7, 32, [64, 136, 8, 1000, 72, 96, 520, 264], 768)])
+def test_grouped_forward_vs_oracle(qops, M, r, Ns, K):
+    """Each output of the grouped forward against the oracle, element-wise."""
+    alpha = 32.0
+    x = synth.activations(M, K, 1950 + M)
+    ws, As, Bs = [], [], []
+    for i, N in enumerate(Ns):
+        ws.append(synth.weight(N, K, 1960 + i))
+        A, B = synth.adapters(N, K, max(r, 1), 1970 + i, 1980 + i)
+        As.append(A)
+        Bs.append(B)
+    qws = [gpu_quant(qops, w) for w in ws]
+    outs = qops.lora_fwd_grouped(dev(x), qws, [dev(a) for a in As] if r else None,
+                                 [dev(b) for b in Bs] if r else None, alpha)
+    xf = to_f64(x)
+    for i, (w, out) in enumerate(zip(ws, outs)):
+        wd = _oracle_weight(w)
+        ref = gemm.lora_forward(x, wd, As[i], Bs[i], alpha, r)
+        got = to_f64(host_bits(out))
+        S = np.abs(xf) @ np.abs(to_f64(wd)).T
+        T = (np.abs(xf @ to_f64(As[i]).T) @ np.abs(to_f64(Bs[i])).T) if r else np.zeros_like(S)
+        assert _oracle_bound_ok(got, ref, S, T, alpha / max(r, 1)) == 0, i
+        assert rel_fro(got, ref) <= TIGHT, i
