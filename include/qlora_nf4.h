@@ -127,6 +127,14 @@ int qlora_nf4_dequant(const uint8_t* packed, const int8_t* qscale,
  * qlora_nf4_bwd_dx (op = 1) or qlora_lora_grad (op = 2) needs for these
  * sizes; 0 when none is needed. Returns 0 for invalid sizes as well (the call
  * itself reports the error).
+ *
+ * Every workspace that is used at all begins with 16 KB of arrival counters
+ * (the decode-shaped kernels add their split partial sums in a fixed order
+ * once the last split of a tile has arrived). They must be zero when a call
+ * starts, and every call leaves them zero when it completes: zero-fill a
+ * workspace once after allocating it (e.g. hipMemset) and it stays valid for
+ * any sequence of calls on one stream, of any entry point. Calls that run at
+ * the same time need separate workspaces.
  */
 size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r);
 
@@ -161,10 +169,13 @@ int qlora_nf4_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K,
 /*
  * Forward of several QLoRA linears that share their input (e.g. the q, k and
  * v projections of one layer), as qlora_nf4_lora_fwd on each weight i:
- *     y[i] = bf16( x . W_i'^T + (alpha / r) . bf16(x . A_i^T) . B_i^T )
- * For M <= 16 the weights are streamed by one launch (their down-projections
- * first), so the launch ramp is paid once; larger M runs the tiled forward
- * per weight. Results are bitwise those of the single call.
+ *     y[i] = bf16( x . W_i'^T + (alpha / r) . (x . A_i^T) . B_i^T )
+ * For M <= 16 the weights are streamed by one launch of the decode-shaped
+ * kernel (qlora_nf4_lora_fwd_batched with x repeated), so the launch ramp is
+ * paid once; larger M runs the tiled forward per weight. The decode kernel
+ * chooses its split of K from the whole group, so results can differ from
+ * the single calls in the fp32 summation order (both within the tolerance of
+ * the single call; repeated identical calls are bitwise identical).
  *   x        [M, K] bf16 (device); G in 1..8.
  *   packed, qscale, step, N, A, B, y  host arrays of G entries: the device
  *            pointers of weight i's stored format (N[i] rows), its adapters
@@ -182,6 +193,42 @@ int qlora_nf4_lora_fwd_grouped(const uint16_t* x, int64_t M, int64_t K, int G,
                                const uint16_t* const* B, int r, float alpha,
                                uint16_t* const* y, void* workspace,
                                size_t ws_bytes, void* stream);
+
+/*
+ * Forward of G independent QLoRA linears in as few launches as possible
+ * (decode shapes: one launch per 32 weights, streaming all of them), e.g. the
+ * linears of a model that do not depend on one another at a decode step, or
+ * many small requests against different weights. For each i:
+ *     y[i] = bf16( x[i] . W_i'^T + (alpha / r) . (x[i] . A_i^T) . B_i^T )
+ * exactly as qlora_nf4_lora_fwd computes it ("A 65B fine-tune on the GPU you
+ * already have", figure 2; "QLoRA and Quantized Training", "In code").
+ *   G        1 .. QLORA_MAX_BATCH weights; M >= 1 rows for every weight.
+ *   x, N, K, packed, qscale, step, A, B, y  host arrays of G entries: weight
+ *            i's input x[i] [M, K[i]] bf16 (device), its shape N[i] x K[i]
+ *            (each within the limits of qlora_nf4_lora_fwd), its stored
+ *            format, adapters A[i] [r, K[i]], B[i] [N[i], r] (the arrays A
+ *            and B may be NULL with r = 0) and its output y[i] [M, N[i]].
+ *            Inputs may repeat (weights that share x).
+ *   workspace / ws_bytes  at least qlora_workspace_bytes_batched(G, M, N, K,
+ *            r) bytes, with the same zero-counter rule as every workspace
+ *            (below).
+ * M <= 16 runs the decode-shaped kernel over the whole table; larger M runs
+ * the tiled forward weight by weight.
+ */
+#define QLORA_MAX_BATCH 4096
+int qlora_nf4_lora_fwd_batched(int G, int64_t M, const uint16_t* const* x,
+                               const int64_t* N, const int64_t* K,
+                               const uint8_t* const* packed,
+                               const int8_t* const* qscale,
+                               const float* const* step,
+                               const uint16_t* const* A,
+                               const uint16_t* const* B, int r, float alpha,
+                               uint16_t* const* y, void* workspace,
+                               size_t ws_bytes, void* stream);
+
+/* Workspace bytes qlora_nf4_lora_fwd_batched needs (0 for invalid sizes). */
+size_t qlora_workspace_bytes_batched(int G, int64_t M, const int64_t* N,
+                                     const int64_t* K, int r);
 
 /*
  * Backward to the input through the frozen dequantized weight (figure 2 of
@@ -219,7 +266,7 @@ int qlora_nf4_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K,
  *           = 0 overwrites them, 1 adds the gradients to what they hold
  *           (accumulation over micro-batches).
  *   workspace / ws_bytes  at least qlora_workspace_bytes(2, M, N, K, r).
- * Size limits as in qlora_nf4_lora_fwd, and M * max(N, K) <= 2^30.
+ * Size limits as in qlora_nf4_lora_fwd.
  * Products are bf16 x bf16 accumulated in fp32; the result does not depend
  * on scheduling (partial sums are added in a fixed order). Every pointer must
  * be 16-byte aligned. The weight itself is not an argument: neither gradient

@@ -27,6 +27,9 @@ SIGNATURES = [
                                   _vp, _vp, _sz, _vp]),
     ("qlora_nf4_lora_fwd_grouped", _i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32,
                                           _vp, _vp, _sz, _vp]),
+    ("qlora_nf4_lora_fwd_batched", _i32, [_i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32,
+                                          _vp, _vp, _sz, _vp]),
+    ("qlora_workspace_bytes_batched", _sz, [_i32, _i64, _vp, _vp, _i32]),
     ("qlora_nf4_bwd_dx", _i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _f32,
                                 _vp, _vp, _sz, _vp]),
     ("qlora_q4_quantize", _i32, [_vp, _i32, _i64, _i32, _vp, _vp, _vp, _vp, _vp]),

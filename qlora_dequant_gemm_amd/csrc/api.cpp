@@ -177,13 +177,54 @@ int qlora_nf4_lora_fwd_grouped(const uint16_t* x, int64_t M, int64_t K, int G, c
     if (st) return st;
     nmax = N[i] > nmax ? N[i] : nmax;
   }
+  // the documented requirement, G times the single call's at the largest N,
+  // is never less than what the grouped launch uses
   const size_t per = qnf4::ws_layout(0, M, nmax, K, r).total;
   const int st = check_ws(workspace, ws_bytes, per * static_cast<size_t>(G));
   if (st) return st;
   const qnf4::Codebook* cb = qnf4::codebook();
   if (!cb) return QLORA_ERR_INIT;
-  return hip_status(qnf4::launch_lora_fwd_grouped(x, M, K, G, packed, qscale, step, N, A, B, r, alpha, y, workspace,
-                                                  per, *cb, as_stream(stream)));
+  const uint16_t* xs[qnf4::kMaxGroups];
+  int64_t Ks[qnf4::kMaxGroups];
+  for (int i = 0; i < G; ++i) {
+    xs[i] = x;
+    Ks[i] = K;
+  }
+  return hip_status(qnf4::launch_lora_fwd_batched(M, G, xs, N, Ks, packed, qscale, step, A, B, r, alpha, y,
+                                                  workspace, *cb, as_stream(stream)));
+}
+
+size_t qlora_workspace_bytes_batched(int G, int64_t M, const int64_t* N, const int64_t* K, int r) {
+  if (G < 1 || G > QLORA_MAX_BATCH || !N || !K || r < 0 || r > QLORA_MAX_RANK) return 0;
+  for (int i = 0; i < G; ++i)
+    if (check_mm(M, N[i], K[i])) return 0;
+  return qnf4::batched_ws_bytes(M, G, N, K, r);
+}
+
+int qlora_nf4_lora_fwd_batched(int G, int64_t M, const uint16_t* const* x, const int64_t* N, const int64_t* K,
+                               const uint8_t* const* packed, const int8_t* const* qscale,
+                               const float* const* step, const uint16_t* const* A, const uint16_t* const* B,
+                               int r, float alpha, uint16_t* const* y, void* workspace, size_t ws_bytes,
+                               void* stream) {
+  if (!x || !N || !K || !packed || !qscale || !step || !y) return QLORA_ERR_NULL;
+  if (G < 1 || G > QLORA_MAX_BATCH) return QLORA_ERR_SHAPE;
+  if (r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_RANK;
+  if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
+  for (int i = 0; i < G; ++i) {
+    int st = check_weight(packed[i], qscale[i], step[i]);
+    if (st) return st;
+    if (!x[i] || !y[i]) return QLORA_ERR_NULL;
+    if (check_mm(M, N[i], K[i])) return QLORA_ERR_SHAPE;
+    if (!aligned16(x[i]) || !aligned16(y[i])) return QLORA_ERR_ALIGN;
+    st = check_adapter(r ? A[i] : nullptr, r ? B[i] : nullptr, r);
+    if (st) return st;
+  }
+  const int st = check_ws(workspace, ws_bytes, qnf4::batched_ws_bytes(M, G, N, K, r));
+  if (st) return st;
+  const qnf4::Codebook* cb = qnf4::codebook();
+  if (!cb) return QLORA_ERR_INIT;
+  return hip_status(qnf4::launch_lora_fwd_batched(M, G, x, N, K, packed, qscale, step, A, B, r, alpha, y, workspace,
+                                                  *cb, as_stream(stream)));
 }
 
 int qlora_nf4_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
@@ -261,8 +302,6 @@ int qlora_lora_grad(const uint16_t* x, const uint16_t* dy, int64_t M, int64_t N,
                     size_t ws_bytes, void* stream) {
   if (!x || !dy || !dA || !dB) return QLORA_ERR_NULL;
   if (N % 8 != 0 || check_mm(M, N, K)) return QLORA_ERR_SHAPE;
-  // one row split of x or dY is addressed by one 32-bit descriptor
-  if (M * (N > K ? N : K) > (int64_t{1} << 30)) return QLORA_ERR_SHAPE;
   if (r < 1 || r > QLORA_MAX_RANK) return QLORA_ERR_RANK;
   if (!A || !B) return QLORA_ERR_NULL;
   if (accumulate != 0 && accumulate != 1) return QLORA_ERR_SHAPE;

@@ -6,11 +6,7 @@
 // right before the multiply ("A 65B fine-tune on the GPU you already have",
 // figure 2; "QLoRA Explained", "What is QLoRA?").
 //
-// Kernels
-//   k_lora_down   rank-r down projection (t or u) on 16x16x32 bf16 MFMA.
-//   k_gemv_fwd    M <= 16: 16 weight rows per workgroup, 8 waves splitting K;
-//                 each lane dequantizes one 64-block straight into the MFMA
-//                 B-operand registers (no LDS); HBM-bound.
+// Kernels (M > 16; the decode shapes have their own kernels)
 //   k_gemm_fwd    M > 16: 256x256 output tile, 4 waves each owning 64 output
 //                 columns; each lane dequantizes its MFMA B operands straight
 //                 into registers, x goes through double-buffered LDS; 32x32x16
@@ -19,8 +15,7 @@
 //   k_gemm_bwd    M > 16: same tiling over dX [M, K]; the contraction runs over
 //                 W's rows, so the dequantized tile is stored row-major and
 //                 read transposed with ds_read_b64_tr_b16.
-//   k_bwd_small   M <= 16 backward: 64-column tiles, row slices reduced by
-//   k_bwd_finish  a second kernel that also adds the LoRA term.
+// The rank-r down projections t and u come from k_down (lora.hip).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -713,6 +708,8 @@ hipError_t launch_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K, c
                            const int8_t* qscale, const float* step, const uint16_t* A, const uint16_t* B,
                            int r, float alpha, uint16_t* y, void* ws, const Codebook& cb,
                            hipStream_t stream) {
+  if (M <= kSmallM)
+    return launch_dec_fwd(M, 1, &x, &N, &K, &packed, &qscale, &step, &A, &B, r, alpha, &y, ws, cb, stream);
   const WsLayout L = ws_layout(0, M, N, K, r);
   char* wsb = static_cast<char*>(ws);
   const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
@@ -723,9 +720,6 @@ hipError_t launch_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K, c
                                           reinterpret_cast<float*>(wsb + L.dp_off));
     if (e != hipSuccess) return e;
   }
-  if (M <= kSmallM)
-    return launch_fwd_small(x, M, N, K, packed, qscale, step, static_cast<const float*>(lora),
-                            static_cast<int>(lora_splits(M, K)), rp, B, r, scale, y, cb, stream);
   const int64_t tiles = cdiv(M, kTile) * cdiv(N, kTile);
   if (K % 256 == 0)
     hipLaunchKernelGGL(k_gemm_fwd<true>, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, x, M, N, K,
@@ -736,40 +730,28 @@ hipError_t launch_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K, c
   return hipGetLastError();
 }
 
-// Weights sharing x: decode shapes compute every weight's t, then run one
-// grouped GEMV launch; larger M runs the tiled forward per weight (launch
-// overhead is negligible there). per_group_ws: bytes of workspace per weight.
-hipError_t launch_lora_fwd_grouped(const uint16_t* x, int64_t M, int64_t K, int G, const uint8_t* const* packed,
-                                   const int8_t* const* qscale, const float* const* step, const int64_t* N,
-                                   const uint16_t* const* A, const uint16_t* const* B, int r, float alpha,
-                                   uint16_t* const* y, void* ws, size_t per_group_ws, const Codebook& cb,
-                                   hipStream_t stream) {
-  char* wsb = static_cast<char*>(ws);
-  if (M > kSmallM) {
-    for (int i = 0; i < G; ++i) {
-      const hipError_t e = launch_lora_fwd(x, M, N[i], K, packed[i], qscale[i], step[i], r ? A[i] : nullptr,
-                                           r ? B[i] : nullptr, r, alpha, y[i], ws, cb, stream);
-      if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
-  }
-  const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
-  const int rp = r > 0 ? static_cast<int>(rank_pad(r)) : 0;
-  GemvGroups grp{};
-  grp.count = G;
-  int64_t wg = 0;
+size_t batched_ws_bytes(int64_t M, int G, const int64_t* N, const int64_t* K, int r) {
+  if (M <= kSmallM) return dec_workspace_bytes(M, G, N, K);
+  size_t need = 0;
   for (int i = 0; i < G; ++i) {
-    float* tpart = nullptr;
-    if (r > 0) {
-      const WsLayout L = ws_layout(0, M, N[i], K, r);
-      tpart = reinterpret_cast<float*>(wsb + i * per_group_ws + L.lora_off);
-      const hipError_t e = launch_lora_down(true, x, M, K, A[i], r, tpart, stream, nullptr, nullptr);
-      if (e != hipSuccess) return e;
-    }
-    grp.g[i] = GemvGroup{packed[i], qscale[i], step[i], tpart, r ? B[i] : nullptr, y[i], N[i], wg};
-    wg += cdiv(N[i], 16);
+    const size_t b = ws_layout(0, M, N[i], K[i], r).total;
+    need = b > need ? b : need;
   }
-  return launch_fwd_small_grouped(x, M, K, grp, static_cast<int>(lora_splits(M, K)), rp, r, scale, cb, stream);
+  return need;
+}
+
+hipError_t launch_lora_fwd_batched(int64_t M, int G, const uint16_t* const* x, const int64_t* N, const int64_t* K,
+                                   const uint8_t* const* packed, const int8_t* const* qscale,
+                                   const float* const* step, const uint16_t* const* A, const uint16_t* const* B,
+                                   int r, float alpha, uint16_t* const* y, void* ws, const Codebook& cb,
+                                   hipStream_t stream) {
+  if (M <= kSmallM) return launch_dec_fwd(M, G, x, N, K, packed, qscale, step, A, B, r, alpha, y, ws, cb, stream);
+  for (int i = 0; i < G; ++i) {
+    const hipError_t e = launch_lora_fwd(x[i], M, N[i], K[i], packed[i], qscale[i], step[i], r ? A[i] : nullptr,
+                                         r ? B[i] : nullptr, r, alpha, y[i], ws, cb, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K, const uint8_t* packed,

@@ -226,7 +226,7 @@ GradPlan grad_plan(int64_t M, int64_t N, int64_t K, int r) {
   };
   g.SB = splits(N);
   g.SA = splits(K);
-  size_t off = 0;
+  size_t off = kWsCounterBytes;                 // the workspace's counter region is left alone
   auto take = [&](size_t bytes) {
     const size_t o = off;
     off += align256(bytes);

@@ -7,12 +7,19 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "codebook.hpp"
 
 namespace qnf4 {
 
 // M at or below this uses the GEMV-shaped kernels (decode shapes).
 constexpr int64_t kSmallM = 16;
+
+// Every workspace that is used at all starts with this many bytes of arrival
+// counters (split-K fix-ups): zero before a call, left zero by every call.
+// The other parts of a workspace layout follow it.
+constexpr size_t kWsCounterBytes = 16384;
 
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
@@ -21,13 +28,46 @@ inline size_t align256(size_t b) { return (b + 255) & ~static_cast<size_t>(255);
 // LoRA rank padded to the 32-deep MFMA contraction used by the epilogues.
 inline int64_t rank_pad(int r) { return round_up(r, 32); }
 
-// Number of K-slices the rank-r down-projection t = in . W^T is split into
-// (fp32 partials summed by the consumer). One slice for the large-M path.
-inline int64_t lora_splits(int64_t M, int64_t Kc) {
-  if (M > kSmallM) return 1;
-  const int64_t s = cdiv(Kc, 64);
-  return s < 16 ? (s < 1 ? 1 : s) : 16;
-}
+// ---------------------------------------------------------------------------
+// Decode-shaped forward (M <= kSmallM) over a table of weights: one launch per
+// chunk of kDecMaxProblems weights (the table travels in the kernel
+// arguments). Items are 256 weight rows x S_p ranges of K.
+// ---------------------------------------------------------------------------
+constexpr int kDecMaxProblems = 32;
+constexpr int kMaxGroups = 8;             // weights of one grouped (shared-x) forward
+constexpr int64_t kDecTargetItems = 1024;
+
+struct DecFwdProblem {
+  const uint16_t* x;        // [M][K]
+  const uint8_t* packed;    // stored weight [N][K]
+  const int8_t* qscale;
+  const float* step;
+  const uint16_t* A;        // [r][K] (r > 0)
+  const uint16_t* B;        // [N][r]
+  uint16_t* y;              // [M][N]
+  int N, K;
+  int item0, S, sps;        // first item; K splits; 256-deep super-steps per split
+  int part0, cnt0;          // first partial slot and counter (S > 1)
+};
+struct DecFwdBatch {
+  DecFwdProblem p[kDecMaxProblems];
+  int count, items, M, r;
+  float scale;
+  float* part;              // [slots][M][256] fp32 partial sums
+  unsigned* cnt;            // arrival counters, one per split row block
+};
+struct DecPlan {
+  std::vector<int> S, sps;
+  int64_t max_slots = 0, max_counters = 0, max_items = 0;
+  size_t part_bytes = 0;
+};
+DecPlan dec_plan(int64_t M, int G, const int64_t* N, const int64_t* K);
+size_t dec_workspace_bytes(int64_t M, int G, const int64_t* N, const int64_t* K);
+// x[i], y[i] etc. are the G weights' operands (host arrays of device pointers)
+hipError_t launch_dec_fwd(int64_t M, int G, const uint16_t* const* x, const int64_t* N, const int64_t* K,
+                          const uint8_t* const* packed, const int8_t* const* qscale, const float* const* step,
+                          const uint16_t* const* A, const uint16_t* const* B, int r, float alpha,
+                          uint16_t* const* y, void* ws, const Codebook& cb, hipStream_t stream);
 
 // Row slices of the small-M backward (fp32 partials of dX): enough column
 // tiles x slices for about one workgroup per CU, 1024 weight rows per step.
@@ -77,27 +117,31 @@ struct WsLayout {
   size_t total = 0;
 };
 
-// op 0: forward (lora contraction over K); op 1: backward (over N).
+// op 0: forward (lora contraction over K); op 1: backward (over N). The
+// decode-shaped forward has its own layout (counters, then split partials).
 inline WsLayout ws_layout(int op, int64_t M, int64_t N, int64_t K, int r) {
   WsLayout w;
+  if (op == 0 && M <= kSmallM) {
+    w.total = dec_workspace_bytes(M, 1, &N, &K);
+    return w;
+  }
   if (r > 0) {
     const int64_t rp = rank_pad(r);
-    const int64_t Kc = op == 0 ? K : N;
     if (M > kSmallM)
       w.lora_bytes = align256(static_cast<size_t>(M * rp * 2));
-    else if (op == 0)
-      w.lora_bytes = align256(static_cast<size_t>(lora_splits(M, Kc) * M * rp * 4));
     else                                       // u partials, one per row slice of the small-M backward
       w.lora_bytes = align256(static_cast<size_t>(bwd_small_splits(N, K) * M * rp * 4));
   }
-  w.part_off = w.lora_bytes;
+  w.lora_off = kWsCounterBytes;
+  w.part_off = w.lora_off + w.lora_bytes;
   if (op == 1 && M <= kSmallM)
     w.part_bytes = align256(static_cast<size_t>(bwd_small_splits(N, K) * M * K * 4));
   w.bt_off = w.part_off + w.part_bytes;
   if (op == 1 && M > kSmallM && r > 0) w.bt_bytes = align256(static_cast<size_t>(r) * N * 2);
   w.dp_off = w.bt_off + w.bt_bytes;
   if (M > kSmallM && r > 0) w.dp_bytes = down_plan(M, op == 0 ? K : N, r).part_bytes;
-  w.total = w.lora_bytes + w.part_bytes + w.bt_bytes + w.dp_bytes;
+  const size_t used = w.lora_bytes + w.part_bytes + w.bt_bytes + w.dp_bytes;
+  w.total = used ? kWsCounterBytes + used : 0;
   return w;
 }
 
@@ -120,45 +164,28 @@ hipError_t launch_dequant(const uint8_t* packed, const int8_t* qscale, const flo
                           uint16_t* out, const Codebook& cb, hipStream_t stream, const float* absmax = nullptr);
 
 // rank-r down projection of `in` [M][Kc] by the adapter (wrow: A [r][Kc];
-// else B [Kc][r]); M <= kSmallM (ldt == 0) writes lora_splits fp32 partials,
-// else bf16 [M][rp]; ldt > 0: bf16 transposed, out [rp][ldt] (ldt = M rounded
-// up to 64, rows past M zero), for any M.
+// else B [Kc][r]); ldt == 0: bf16 [M][rp] (M > kSmallM); ldt > 0: bf16
+// transposed, out [rp][ldt] (ldt = M rounded up to 64, rows past M zero), for
+// any M.
 // wt: workspace for the transposed adapter (bf16 path, wrow == false; r * Kc
 // bf16); part: down_plan(M, Kc, r).part_bytes of workspace (bf16 path).
 hipError_t launch_lora_down(bool wrow, const uint16_t* in, int64_t M, int64_t Kc, const uint16_t* W, int r,
                             void* out, hipStream_t stream, uint16_t* wt, float* part, int64_t ldt = 0);
-hipError_t launch_fwd_small(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
-                            const int8_t* qscale, const float* step, const float* tpart, int St, int rp,
-                            const uint16_t* B, int r, float scale, uint16_t* y, const Codebook& cb,
-                            hipStream_t stream);
-// Grouped decode forward: up to kMaxGroups weights sharing x in one launch.
-constexpr int kMaxGroups = 8;
-struct GemvGroup {
-  const uint8_t* packed;
-  const int8_t* qscale;
-  const float* step;
-  const float* tpart;          // this weight's t partial sums (fp32 [St][M][rp])
-  const uint16_t* B;
-  uint16_t* y;
-  int64_t N;
-  int64_t wg0;                 // first workgroup of this weight
-};
-struct GemvGroups {
-  GemvGroup g[kMaxGroups];
-  int count;
-};
-hipError_t launch_fwd_small_grouped(const uint16_t* x, int64_t M, int64_t K, const GemvGroups& G, int St, int rp,
-                                    int r, float scale, const Codebook& cb, hipStream_t stream);
-hipError_t launch_lora_fwd_grouped(const uint16_t* x, int64_t M, int64_t K, int G, const uint8_t* const* packed,
-                                   const int8_t* const* qscale, const float* const* step, const int64_t* N,
-                                   const uint16_t* const* A, const uint16_t* const* B, int r, float alpha,
-                                   uint16_t* const* y, void* ws, size_t per_group_ws, const Codebook& cb,
-                                   hipStream_t stream);
 hipError_t launch_bwd_small(const uint16_t* dy, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
                             const int8_t* qscale, const float* step, float* upart, int rp, const uint16_t* A,
                             const uint16_t* B, int r, float scale, float* part, uint16_t* dx, const Codebook& cb,
                             hipStream_t stream);
 
+// The forward of G weights, each with its own input x[i] (x[i] may repeat:
+// weights that share their input). Decode shapes run launch_dec_fwd over the
+// whole table; larger M runs the tiled forward per weight, reusing the
+// workspace (batched_ws_bytes of it).
+hipError_t launch_lora_fwd_batched(int64_t M, int G, const uint16_t* const* x, const int64_t* N, const int64_t* K,
+                                   const uint8_t* const* packed, const int8_t* const* qscale,
+                                   const float* const* step, const uint16_t* const* A, const uint16_t* const* B,
+                                   int r, float alpha, uint16_t* const* y, void* ws, const Codebook& cb,
+                                   hipStream_t stream);
+size_t batched_ws_bytes(int64_t M, int G, const int64_t* N, const int64_t* K, int r);
 hipError_t launch_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
                            const int8_t* qscale, const float* step, const uint16_t* A, const uint16_t* B,
                            int r, float alpha, uint16_t* y, void* ws, const Codebook& cb,

@@ -14,21 +14,6 @@
 
 namespace qnf4 {
 
-// 8 consecutive contraction values W(j, k..k+7) of adapter column j.
-template <bool WROW>
-__device__ __forceinline__ u32x4 adapter8(const uint16_t* __restrict__ W, int64_t Kc, int r, int j, int64_t k) {
-  if (j >= r || k >= Kc) return u32x4{0u, 0u, 0u, 0u};
-  if (WROW) return ld16(W + static_cast<int64_t>(j) * Kc + k);   // Kc % 8 == 0, rows 16-byte aligned
-  uint32_t v[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t lo = W[(k + 2 * e) * r + j];
-    const uint32_t hi = W[(k + 2 * e + 1) * r + j];
-    v[e] = lo | (hi << 16);
-  }
-  return u32x4{v[0], v[1], v[2], v[3]};
-}
-
 // ---------------------------------------------------------------------------
 // Large M (and the transposed outputs of the adapter gradients): 64-row tiles
 // x KS splits of the contraction. Wave w owns rows 16w .. 16w + 15 of the
@@ -129,51 +114,6 @@ __global__ __launch_bounds__(256) void k_down_finish(const float* __restrict__ p
   out[ldt ? j * ldt + m : m * rp + j] = bf16_bits(sum);
 }
 
-// ---------------------------------------------------------------------------
-// Small M (<= 16): fp32 partial sums [S][M][rp]. Grid S workgroups of 8 waves;
-// workgroup s owns a contiguous range of 32-deep steps and its waves take
-// them round robin, so every load of the workgroup is issued up front.
-// ---------------------------------------------------------------------------
-template <bool WROW>
-__global__ __launch_bounds__(512) void k_lora_down_small(const uint16_t* __restrict__ in, int64_t M, int64_t Kc,
-                                                         const uint16_t* __restrict__ W, int r, int rp, int S,
-                                                         float* __restrict__ out) {
-  __shared__ f32x4 red[8][8][64];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int g = lane >> 4, c = lane & 15;
-  const int s = blockIdx.x;
-  const int ntile = rp / 16;
-  const int64_t nsteps = cdiv(Kc, 32);
-  const int64_t beg = s * nsteps / S, end = (s + 1) * nsteps / S;
-  const uint16_t* in_row = in + imin(static_cast<int64_t>(c), M - 1) * Kc;
-  f32x4 acc[8];
-#pragma unroll
-  for (int jt = 0; jt < 8; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-  for (int64_t st = beg + w; st < end; st += 8) {
-    const int64_t k = st * 32 + 8 * g;
-    const bf16x8 a = as_bf16x8(k < Kc ? ld16(in_row + k) : u32x4{0u, 0u, 0u, 0u});
-#pragma unroll
-    for (int jt = 0; jt < 8; ++jt)
-      if (jt < ntile) acc[jt] = mfma16(a, as_bf16x8(adapter8<WROW>(W, Kc, r, 16 * jt + c, k)), acc[jt]);
-  }
-#pragma unroll
-  for (int jt = 0; jt < 8; ++jt)
-    if (jt < ntile) red[w][jt][lane] = acc[jt];
-  __syncthreads();
-  for (int idx = t; idx < ntile * 64; idx += 512) {
-    const int jt = idx >> 6, ln = idx & 63;
-    f32x4 sum = red[0][jt][ln];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) sum += red[i][jt][ln];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t m = 4 * (ln >> 4) + v;
-      if (m < M) out[(s * M + m) * rp + 16 * jt + (ln & 15)] = sum[v];
-    }
-  }
-}
-
 // B [N][r] -> Bt [r][N] (the backward contracts over N, so it reads the
 // adapter row-major through this copy): 64 rows of B (one contiguous run of
 // 128 r bytes) staged in LDS, then each rank's 64 values written contiguously.
@@ -196,16 +136,6 @@ __global__ __launch_bounds__(256) void k_adapter_t(const uint16_t* __restrict__ 
 hipError_t launch_lora_down(bool wrow, const uint16_t* in, int64_t M, int64_t Kc, const uint16_t* W, int r,
                             void* out, hipStream_t stream, uint16_t* wt, float* part, int64_t ldt) {
   const int rp = static_cast<int>(rank_pad(r));
-  if (M <= kSmallM && ldt == 0) {
-    const int S = static_cast<int>(lora_splits(M, Kc));
-    if (wrow)
-      hipLaunchKernelGGL(k_lora_down_small<true>, dim3(S), dim3(512), 0, stream, in, M, Kc, W, r, rp, S,
-                         static_cast<float*>(out));
-    else
-      hipLaunchKernelGGL(k_lora_down_small<false>, dim3(S), dim3(512), 0, stream, in, M, Kc, W, r, rp, S,
-                         static_cast<float*>(out));
-    return hipGetLastError();
-  }
   const uint16_t* Wr = W;
   if (!wrow) {
     hipLaunchKernelGGL(k_adapter_t, dim3(static_cast<unsigned>(cdiv(Kc, 64))), dim3(256), 0, stream, W, Kc, r, wt);

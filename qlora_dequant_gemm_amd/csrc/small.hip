@@ -1,14 +1,9 @@
-// Decode-shaped (M <= 16) fused NF4-dequant matmuls for gfx950.
+// Decode-shaped (M <= 16) fused NF4-dequant backward for gfx950.
 //
 // At these shapes every weight is used by at most 16 rows, so the kernels are
-// bound by streaming the 0.516 bytes/param NF4 weight from HBM. They are
-// written to keep as many loads in flight as possible: operands of the next
-// step are loaded while the current one is decoded and multiplied, and the
-// epilogue's inputs are fetched at kernel start.
+// bound by streaming the 0.516 bytes/param NF4 weight from HBM. Operands of
+// the next step are loaded while the current one is decoded and multiplied.
 //
-//   k_gemv_fwd    y = x . W'^T (+ LoRA): 16 weight rows per workgroup, 16 waves
-//                 splitting K; each lane dequantizes one 64-block straight
-//                 into 16x16x32 MFMA B-operand registers.
 //   k_bwd_small   dX partials: 64-column tiles x row slices; 1024 weight rows
 //                 per step dequantized into LDS and read transposed
 //                 (ds_read_b64_tr_b16).
@@ -19,164 +14,6 @@
 #include "mm_common.hpp"
 
 namespace qnf4 {
-
-struct GemvStage {
-  u32x4 p0, p1;      // 32 packed bytes = one 64-block of one weight row
-  u32x4 xa[8];       // the matching 64 activations of one x row
-  float d;
-  int8_t q;
-  bool valid;
-};
-
-// ---------------------------------------------------------------------------
-// k_gemv_fwd. Lane l: g = l/16 selects one of the 4 blocks of a 256-deep
-// super-step, c = l%16 is the weight row (B column) and the x row (A row).
-// Dynamic LDS: rp/32 * kGemvWaves * 64 * 32 bytes for the LoRA t sums.
-// ---------------------------------------------------------------------------
-constexpr int kGemvWaves = 16;
-
-// The body of one workgroup (weight rows n0 .. n0 + 15); the plain kernel and
-// the grouped one (several weights sharing x) differ only in how a workgroup
-// finds its weight and rows.
-__device__ __forceinline__ void gemv_fwd_rows(const uint16_t* __restrict__ x, int64_t M, int64_t N, int64_t K,
-                                              const uint8_t* __restrict__ packed,
-                                              const int8_t* __restrict__ qscale, const float* __restrict__ step,
-                                              const float* __restrict__ tpart, int St, int rp,
-                                              const uint16_t* __restrict__ Bl, int r, float scale,
-                                              uint16_t* __restrict__ y, const Codebook& cb, int64_t n0) {
-  __shared__ f32x4 red[kGemvWaves][64];
-  extern __shared__ f32x4 tred[];            // [wave][js][lane][2]
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int g = lane >> 4, c = lane & 15;
-  const int64_t n = imin(n0 + c, N - 1);
-  const int64_t m = imin(static_cast<int64_t>(c), M - 1);
-  const int64_t nbr = K / 64;
-  const int64_t nss = cdiv(nbr, 4);
-  const uint8_t* prow = packed + n * (K / 2);
-  const uint16_t* xrow = x + m * K;
-  const int njs = r > 0 ? rp / 32 : 0;
-
-  // epilogue operands first (ranks up to 64; larger ranks load the rest after
-  // the main loop): this wave's share of the t partial sums, and (wave 0) the
-  // B rows of the LoRA up-projection
-  constexpr int kPre = 2;
-  f32x4 tv[4][2];
-  u32x4 bop[4];
-#pragma unroll
-  for (int js = 0; js < 4; ++js) {
-    tv[js][0] = tv[js][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bop[js] = u32x4{0u, 0u, 0u, 0u};
-  }
-  const uint16_t* brow = Bl + n * r;
-  auto load_epi = [&](int js) {
-    for (int s = w; s < St; s += kGemvWaves) {
-      const float* tp = tpart + (s * M + m) * rp + 32 * js + 8 * g;
-      tv[js][0] += *reinterpret_cast<const f32x4*>(tp);
-      tv[js][1] += *reinterpret_cast<const f32x4*>(tp + 4);
-    }
-    if (w == 0) bop[js] = load_row8(brow, 32 * js + 8 * g, r, (r & 7) == 0);
-  };
-#pragma unroll
-  for (int js = 0; js < kPre; ++js)
-    if (js < njs) load_epi(js);
-
-  auto load_stage = [&](int64_t ss, GemvStage& st) {
-    const int64_t kb = ss * 4 + g;
-    st.valid = kb < nbr;
-    const int64_t kbc = st.valid ? kb : nbr - 1;
-    st.p0 = ld16(prow + kbc * 32);
-    st.p1 = ld16(prow + kbc * 32 + 16);
-    const int64_t blk = n * nbr + kbc;
-    st.q = qscale[blk];
-    st.d = step[blk >> 8];
-    const uint16_t* xk = xrow + kbc * 64;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) st.xa[j] = ld16(xk + 8 * j);
-  };
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  auto run_stage = [&](const GemvStage& st) {
-    const float sc = st.valid ? block_scale(st.q, st.d) : 0.0f;
-    const MagTable tb = make_table(cb, sc);
-    const uint32_t pw[8] = {st.p0.x, st.p0.y, st.p0.z, st.p0.w, st.p1.x, st.p1.y, st.p1.z, st.p1.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc = mfma16(as_bf16x8(st.xa[j]), as_bf16x8(decode8(pw[j], tb)), acc);
-  };
-  // one super-step per iteration (loads carried across iterations would make
-  // the compiler wait on all of them at the loop head); for K up to 4096
-  // every wave has a single super-step
-  for (int64_t ss = w; ss < nss; ss += kGemvWaves) {
-    GemvStage st;
-    load_stage(ss, st);
-    run_stage(st);
-  }
-
-#pragma unroll
-  for (int js = kPre; js < 4; ++js)
-    if (js < njs) load_epi(js);
-  red[w][lane] = acc;
-#pragma unroll
-  for (int js = 0; js < 4; ++js) {
-    if (js < njs) {
-      tred[((w * njs + js) * 64 + lane) * 2 + 0] = tv[js][0];
-      tred[((w * njs + js) * 64 + lane) * 2 + 1] = tv[js][1];
-    }
-  }
-  __syncthreads();
-  if (w != 0) return;
-  acc = red[0][lane];
-#pragma unroll
-  for (int i = 1; i < kGemvWaves; ++i) acc += red[i][lane];
-  if (njs > 0) {
-    f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int js = 0; js < 4; ++js) {
-      if (js < njs) {
-        f32x4 s0 = tred[((0 * njs + js) * 64 + lane) * 2 + 0];
-        f32x4 s1 = tred[((0 * njs + js) * 64 + lane) * 2 + 1];
-#pragma unroll
-        for (int i = 1; i < kGemvWaves; ++i) {
-          s0 += tred[((i * njs + js) * 64 + lane) * 2 + 0];
-          s1 += tred[((i * njs + js) * 64 + lane) * 2 + 1];
-        }
-        const u32x4 a = {pack_bf16x2(s0.x, s0.y), pack_bf16x2(s0.z, s0.w), pack_bf16x2(s1.x, s1.y),
-                         pack_bf16x2(s1.z, s1.w)};
-        tmp = mfma16(as_bf16x8(a), as_bf16x8(bop[js]), tmp);
-      }
-    }
-    acc += scale * tmp;
-  }
-  const int64_t nn = n0 + c;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int64_t mm = 4 * g + v;
-    if (mm < M && nn < N) y[mm * N + nn] = bf16_bits(acc[v]);
-  }
-}
-
-__global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_fwd(const uint16_t* __restrict__ x, int64_t M, int64_t N,
-                                                  int64_t K, const uint8_t* __restrict__ packed,
-                                                  const int8_t* __restrict__ qscale,
-                                                  const float* __restrict__ step,
-                                                  const float* __restrict__ tpart, int St, int rp,
-                                                  const uint16_t* __restrict__ Bl, int r, float scale,
-                                                  uint16_t* __restrict__ y, Codebook cb) {
-  gemv_fwd_rows(x, M, N, K, packed, qscale, step, tpart, St, rp, Bl, r, scale, y, cb,
-                static_cast<int64_t>(blockIdx.x) * 16);
-}
-
-// Several weights that share x (e.g. the q, k, v projections) in one launch:
-// workgroups [wg0_i, wg0_{i+1}) take weight i's rows 16 at a time.
-__global__ __launch_bounds__(64 * kGemvWaves) void k_gemv_fwd_grouped(const uint16_t* __restrict__ x, int64_t M,
-                                                          int64_t K, int St, int rp, int r, float scale,
-                                                          Codebook cb, GemvGroups G) {
-  int gi = 0;
-#pragma unroll
-  for (int i = 1; i < kMaxGroups; ++i)
-    if (i < G.count && static_cast<int64_t>(blockIdx.x) >= G.g[i].wg0) gi = i;
-  const GemvGroup& q = G.g[gi];
-  gemv_fwd_rows(x, M, q.N, K, q.packed, q.qscale, q.step, q.tpart, St, rp, q.B, r, scale, q.y, cb,
-                (static_cast<int64_t>(blockIdx.x) - q.wg0) * 16);
-}
 
 // ---------------------------------------------------------------------------
 // k_bwd_small: grid (K/64 column tiles, S row slices), 16 waves. Each step
@@ -382,27 +219,6 @@ __global__ __launch_bounds__(256) void k_bwd_finish(const float* __restrict__ pa
 // ---------------------------------------------------------------------------
 // launchers (M <= 16)
 // ---------------------------------------------------------------------------
-hipError_t launch_fwd_small(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
-                            const int8_t* qscale, const float* step, const float* tpart, int St, int rp,
-                            const uint16_t* B, int r, float scale, uint16_t* y, const Codebook& cb,
-                            hipStream_t stream) {
-  const size_t lds = r > 0 ? static_cast<size_t>(rp / 32) * kGemvWaves * 64 * 32 : 0;
-  hipLaunchKernelGGL(k_gemv_fwd, dim3(static_cast<unsigned>(cdiv(N, 16))), dim3(64 * kGemvWaves), lds, stream, x, M,
-                     N, K,
-                     packed, qscale, step, tpart, St, rp, B, r, scale, y, cb);
-  return hipGetLastError();
-}
-
-hipError_t launch_fwd_small_grouped(const uint16_t* x, int64_t M, int64_t K, const GemvGroups& G, int St, int rp,
-                                    int r, float scale, const Codebook& cb, hipStream_t stream) {
-  const size_t lds = r > 0 ? static_cast<size_t>(rp / 32) * kGemvWaves * 64 * 32 : 0;
-  int64_t wgs = 0;
-  for (int i = 0; i < G.count; ++i) wgs += cdiv(G.g[i].N, 16);
-  hipLaunchKernelGGL(k_gemv_fwd_grouped, dim3(static_cast<unsigned>(wgs)), dim3(64 * kGemvWaves), lds, stream, x, M,
-                     K, St, rp, r, scale, cb, G);
-  return hipGetLastError();
-}
-
 hipError_t launch_bwd_small(const uint16_t* dy, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
                             const int8_t* qscale, const float* step, float* upart, int rp, const uint16_t* A,
                             const uint16_t* B, int r, float scale, float* part, uint16_t* dx, const Codebook& cb,

@@ -146,7 +146,11 @@ def workspace_bytes(op, M, N, K, r):
 
 
 class Workspace:
-    """Grow-only device scratch buffer reused across calls on one stream."""
+    """Grow-only device scratch buffer reused across calls on one stream.
+
+    Zero-filled when allocated: a workspace starts with the arrival counters
+    of the split-K fix-ups, which must be zero before a call and are left zero
+    by every call."""
 
     def __init__(self, device="cuda"):
         self.device = device
@@ -156,7 +160,7 @@ class Workspace:
         if nbytes == 0:
             return None
         if self.buf is None or self.buf.numel() < nbytes:
-            self.buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=self.device)
+            self.buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=self.device)
         return self.buf
 
 
@@ -261,6 +265,50 @@ def lora_fwd_grouped(x, qws, As=None, Bs=None, alpha=0.0, outs=None, ws=None):
         _ptr(x), M, K, G, arr([q.packed for q in qws]), arr([q.qscale for q in qws]), arr([q.step for q in qws]),
         (ctypes.c_int64 * G)(*Ns), arr(As) if r else None, arr(Bs) if r else None, r, float(alpha), arr(outs),
         _ptr(wsb), 0 if wsb is None else wsb.numel(), _stream(x.device)))
+    return outs
+
+
+def lora_fwd_batched(xs, qws, As=None, Bs=None, alpha=0.0, outs=None, ws=None):
+    """The forward of independent linears, each with its own input:
+    [x_i . deq(W_i)^T + (alpha/r) . (x_i . A_i^T) . B_i^T for each i], every x_i
+    [M, K_i] with one M. Decode shapes stream all weights in one launch per
+    32 of them."""
+    G = len(qws)
+    if len(xs) != G:
+        raise ValueError("one input per weight")
+    if (As is None) != (Bs is None) or (As is not None and (len(As) != G or len(Bs) != G)):
+        raise ValueError("As and Bs must both be None or both hold one adapter per weight")
+    if outs is not None and len(outs) != G:
+        raise ValueError("one output per weight")
+    M = _rows(xs[0], "xs[0]")
+    ranks = set()
+    for i, (x, qw) in enumerate(zip(xs, qws)):
+        N, K = qw.shape
+        _shape(x, (M, K), f"xs[{i}]")
+        ranks.add(_adapter_rank(As[i] if As is not None else None, Bs[i] if Bs is not None else None, N, K))
+        if outs is not None:
+            _shape(outs[i], (M, N), f"outs[{i}]")
+    if len(ranks) != 1:
+        raise ValueError("every weight must have adapters of one rank")
+    r = ranks.pop()
+    dev = xs[0].device
+    for i, (x, qw) in enumerate(zip(xs, qws)):
+        _need(x, torch.bfloat16, f"xs[{i}]", dev)
+        _check_weight(qw, dev)
+        _check_adapters(As[i] if As is not None else None, Bs[i] if Bs is not None else None, qw.shape[0],
+                        qw.shape[1], dev)
+    if outs is None:
+        outs = [torch.empty((M, qw.shape[0]), dtype=torch.bfloat16, device=dev) for qw in qws]
+    outs = [_check_out(o, (M, qw.shape[0]), dev, f"outs[{i}]") for i, (o, qw) in enumerate(zip(outs, qws))]
+    arr = lambda ts: (ctypes.c_void_p * G)(*[t.data_ptr() if t is not None else 0 for t in ts])
+    Ns = (ctypes.c_int64 * G)(*[qw.shape[0] for qw in qws])
+    Ks = (ctypes.c_int64 * G)(*[qw.shape[1] for qw in qws])
+    need = int(_lib.lib().qlora_workspace_bytes_batched(G, M, Ns, Ks, r))
+    wsb = (ws or Workspace(dev)).get(need)
+    _lib.check("qlora_nf4_lora_fwd_batched", _lib.lib().qlora_nf4_lora_fwd_batched(
+        G, M, arr(xs), Ns, Ks, arr([q.packed for q in qws]), arr([q.qscale for q in qws]),
+        arr([q.step for q in qws]), arr(As) if r else None, arr(Bs) if r else None, r, float(alpha), arr(outs),
+        _ptr(wsb), 0 if wsb is None else wsb.numel(), _stream(dev)))
     return outs
 
 

@@ -79,10 +79,15 @@ def test_format_calls_reject_bad_arguments():
 
 def test_workspace_sizes():
     ws = ops.workspace_bytes
+    C = 16384                                                     # arrival counters open every workspace
     assert ws(0, 4096, 11008, 4096, 0) == 0
     # bf16 t (rank padded to 32) + fp32 partials of 4 contraction splits (16 ranks)
-    assert ws(0, 4096, 11008, 4096, 16) == 4096 * 32 * 2 + 4 * 4096 * 16 * 4
-    assert ws(0, 16, 4096, 4096, 16) == 16 * 16 * 32 * 4          # 16 K-slices of fp32 partials
+    assert ws(0, 4096, 11008, 4096, 16) == C + 4096 * 32 * 2 + 4 * 4096 * 16 * 4
+    # decode shapes: 16 row blocks of 256 x 8 splits of K (two 256-deep steps
+    # each at M = 16) of fp32 partials [M][256]; one split needs nothing
+    assert ws(0, 16, 4096, 4096, 16) == C + 16 * 8 * 16 * 256 * 4
+    assert ws(0, 1, 4096, 4096, 16) == C + 16 * 16 * 1 * 256 * 4
+    assert ws(0, 16, 8, 64, 8) == 0
     assert ws(1, 16, 4096, 4096, 0) > 0                           # small-M backward partials
     assert ws(1, 4096, 4096, 11008, 0) == 0
     assert ws(2, 16, 16, 64, 0) == 0 and ws(0, 0, 16, 64, 0) == 0
@@ -92,9 +97,17 @@ def test_workspace_sizes():
     # 64), and the fp32 partials of the dY and x contractions
     assert ws(3, 16, 16, 64, 8) == 0 and ws(2, 16, 16, 64, 129) == 0
     g = ws(2, 4096, 11008, 4096, 16)
-    fixed = 16 * 11008 * 2 + 2 * 32 * 4096 * 2
+    fixed = C + 16 * 11008 * 2 + 2 * 32 * 4096 * 2
     assert g >= fixed + 11008 * 16 * 4 + 4096 * 16 * 4
     assert g <= fixed + 64 * (11008 + 4096) * 16 * 4 + 5 * 256
+    # the batched forward: one launch per 32 weights reuses one region
+    N = (ctypes.c_int64 * 3)(4096, 11008, 4096)
+    K = (ctypes.c_int64 * 3)(4096, 4096, 11008)
+    b = _lib.lib().qlora_workspace_bytes_batched(3, 16, N, K, 16)
+    assert b >= C and (b - C) % (16 * 256 * 4) == 0
+    assert _lib.lib().qlora_workspace_bytes_batched(3, 4096, N, K, 16) == max(ws(0, 4096, n, k, 16)
+                                                                               for n, k in zip(N, K))
+    assert _lib.lib().qlora_workspace_bytes_batched(0, 16, N, K, 16) == 0
 
 
 V = ctypes.c_void_p
@@ -123,8 +136,10 @@ def _bwd(dy=FAKE, M=16, N=64, K=64, packed=FAKE, q=FAKE, step=FAKE, A=V(0), B=V(
     (dict(r=8), 1), (dict(r=8, A=FAKE), 1), (dict(A=FAKE), 4), (dict(r=-1), 4),
     (dict(r=129, A=FAKE, B=FAKE), 4),
     (dict(r=8, A=ODD, B=FAKE, ws=FAKE, wsb=1 << 20), 3),
-    (dict(r=8, A=FAKE, B=FAKE), 5), (dict(r=8, A=FAKE, B=FAKE, ws=FAKE, wsb=16), 5),
-    (dict(r=8, A=FAKE, B=FAKE, ws=ODD, wsb=1 << 20), 3),
+    # K = 1024 at M = 16: the decode kernel splits K, so a workspace is needed
+    (dict(r=8, A=FAKE, B=FAKE, K=1024), 5), (dict(r=8, A=FAKE, B=FAKE, ws=FAKE, wsb=16, K=1024), 5),
+    (dict(r=8, A=FAKE, B=FAKE, ws=ODD, wsb=1 << 20, K=1024), 3),
+    (dict(M=300, r=8, A=FAKE, B=FAKE), 5),
 ])
 def test_forward_rejects_bad_arguments(kwargs, status):
     assert _fwd(**kwargs) == status
@@ -188,7 +203,7 @@ def test_grouped_forward_rejects_bad_arguments():
     assert call(G=0) == 2 and call(G=9) == 2 and call(K=96) == 2 and call(n=N(64, 0)) == 2
     assert call(x=V(0)) == 1 and call(pk=P(f, 0)) == 1 and call(y=P(f, 0)) == 1 and call(r=8) == 1
     assert call(y=P(f, o)) == 3 and call(pk=P(o, f)) == 3 and call(r=129, A=P(f, f), B=P(f, f)) == 4
-    assert call(r=8, A=P(f, f), B=P(f, f)) == 5      # workspace needed for the adapters' t
+    assert call(r=8, A=P(f, f), B=P(f, f), K=1024) == 5    # workspace needed for the split of K
 
 
 def test_quantize_dq_dequant_reject_bad_arguments():
@@ -222,13 +237,12 @@ def test_thresholds_sit_well_inside_quantize_cells():
 def test_size_limits_return_shape_errors():
     """Sizes the kernels' 32-bit buffer descriptors or tile numbering cannot
     address are rejected before anything is launched (N, K <= 2^21; the 256 x
-    256 tile count below 2^31; for the adapter gradients M * max(N, K) <= 2^30)."""
+    256 tile count below 2^31)."""
     big = 1 << 21
     assert _fwd(N=big + 64, K=64) == 2 and _fwd(K=big + 64) == 2
     assert _fwd(M=(1 << 31) + 1) == 2
     assert _fwd(M=1 << 31, N=big, K=64) == 2                    # 2^23 x 2^13 tiles
     assert _bwd(N=big + 8, K=64, wsb=0, ws=V(0)) == 2 and _bwd(K=big + 64, wsb=0, ws=V(0)) == 2
-    assert _grad(M=1 << 20, N=2048, K=64) == 2                  # 2^31 > 2^30
     assert _lib.lib().qlora_nf4_merge(FAKE, FAKE, FAKE, big + 1, 64, V(0), V(0), 0, 0.0, FAKE, V(0)) == 2
     assert _lib.lib().qlora_dq_scales(FAKE, 1 << 31, FAKE, FAKE, V(0)) == 2
     # the largest accepted sizes pass the shape checks (and stop at the

@@ -691,7 +691,9 @@ def test_format_error_ordering_on_7b_weight(qops):
 # grouped forward of weights that share x
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("M,r", [(1, 16), (5, 0), (16, 16), (40, 16)])
-def test_grouped_forward_equals_single_calls(qops, M, r):
+def test_grouped_forward_equals_batched_and_repeats(qops, M, r):
+    """The grouped forward is the batched forward with x repeated (the same
+    plan, so bitwise equal), and repeated calls are bitwise identical."""
     K, Ns = 512, [512, 200, 64]
     x = dev(synth.activations(M, K, 950))
     qws, As, Bs = [], [], []
@@ -701,21 +703,31 @@ def test_grouped_forward_equals_single_calls(qops, M, r):
         As.append(dev(A) if r else None)
         Bs.append(dev(B) if r else None)
     outs = qops.lora_fwd_grouped(x, qws, As if r else None, Bs if r else None, 32.0)
+    again = qops.lora_fwd_grouped(x, qws, As if r else None, Bs if r else None, 32.0)
+    bat = qops.lora_fwd_batched([x] * 3, qws, As if r else None, Bs if r else None, 32.0)
     for i in range(3):
-        one = qops.lora_fwd(x, qws[i], As[i], Bs[i], 32.0)
-        assert torch.equal(outs[i].view(torch.int16), one.view(torch.int16)), i
+        assert torch.equal(outs[i].view(torch.int16), again[i].view(torch.int16)), i
+        assert torch.equal(outs[i].view(torch.int16), bat[i].view(torch.int16)), i
 
 
 def test_grouped_forward_7b_qkv(qops):
+    """q, k, v of one 7B layer at M = 16 in one grouped call, each output
+    against the oracle element-wise."""
     c = synth.CONFIGS["7b_attn"]
     N, K, r, alpha = c["N"], c["K"], c["r"], c["alpha"]
-    x = dev(synth.activations(16, K, 990))
-    qws = [gpu_quant(qops, synth.weight(N, K, 991 + i)) for i in range(3)]
+    x = synth.activations(16, K, 990)
+    ws = [synth.weight(N, K, 991 + i) for i in range(3)]
     ad = [synth.adapters(N, K, r, 995 + i, 998 + i) for i in range(3)]
-    As, Bs = [dev(a) for a, _ in ad], [dev(b) for _, b in ad]
-    outs = qops.lora_fwd_grouped(x, qws, As, Bs, alpha)
+    outs = qops.lora_fwd_grouped(dev(x), [gpu_quant(qops, w) for w in ws], [dev(a) for a, _ in ad],
+                                 [dev(b) for _, b in ad], alpha)
+    xf = to_f64(x)
     for i in range(3):
-        assert torch.equal(outs[i].view(torch.int16), qops.lora_fwd(x, qws[i], As[i], Bs[i], alpha).view(torch.int16))
+        wd = _oracle_weight(ws[i])
+        ref = gemm.lora_forward(x, wd, ad[i][0], ad[i][1], alpha, r)
+        got = to_f64(host_bits(outs[i]))
+        S = np.abs(xf) @ np.abs(to_f64(wd)).T
+        T = np.abs(xf @ to_f64(ad[i][0]).T) @ np.abs(to_f64(ad[i][1])).T
+        assert _oracle_bound_ok(got, ref, S, T, alpha / r) == 0, i
 
 
 # ---------------------------------------------------------------------------
@@ -802,3 +814,56 @@ def test_grouped_forward_vs_oracle(qops, M, r, Ns, K):
         T = (np.abs(xf @ to_f64(As[i]).T) @ np.abs(to_f64(Bs[i])).T) if r else np.zeros_like(S)
         assert _oracle_bound_ok(got, ref, S, T, alpha / max(r, 1)) == 0, i
         assert rel_fro(got, ref) <= TIGHT, i
+
+
+# ---------------------------------------------------------------------------
+# batched forward: independent inputs and shapes per weight in one call
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,r,G,seed", [(1, 16, 5, 0), (16, 16, 7, 1), (4, 0, 3, 2), (3, 5, 4, 3),
+                                        (16, 64, 3, 4), (8, 128, 2, 5), (2, 32, 40, 6), (40, 16, 3, 7)])
+def test_batched_forward_vs_oracle(qops, M, r, G, seed):
+    """Weights of mixed shapes (K = 64 .. 11008, ragged N), each with its own
+    x: every output against the oracle element-wise. G = 40 spans two
+    launches (32 weights per launch); M = 40 takes the tiled path."""
+    rng = np.random.Generator(np.random.PCG64(3000 + seed))
+    shapes = [(int(rng.choice([8, 64, 136, 520, 1000, 4096])), int(rng.choice([64, 320, 1024, 4096, 11008])))
+              for _ in range(G)]
+    if G >= 3:
+        shapes[0], shapes[1] = (4096, 4096), (1000, 11008)
+    if G > 8:
+        shapes = [(n, min(k, 1024)) for n, k in shapes]
+    alpha = 16.0
+    xs, ws, As, Bs = [], [], [], []
+    for i, (N, K) in enumerate(shapes):
+        xs.append(synth.activations(M, K, 3100 + 10 * seed + i))
+        ws.append(synth.weight(N, K, 3200 + 10 * seed + i))
+        A, B = synth.adapters(N, K, max(r, 1), 3300 + i, 3400 + i)
+        As.append(A)
+        Bs.append(B)
+    outs = qops.lora_fwd_batched([dev(x) for x in xs], [gpu_quant(qops, w) for w in ws],
+                                 [dev(a) for a in As] if r else None, [dev(b) for b in Bs] if r else None, alpha)
+    for i, (N, K) in enumerate(shapes):
+        wd = _oracle_weight(ws[i])
+        ref = gemm.lora_forward(xs[i], wd, As[i], Bs[i], alpha, r)
+        got = to_f64(host_bits(outs[i]))
+        xf = to_f64(xs[i])
+        S = np.abs(xf) @ np.abs(to_f64(wd)).T
+        T = (np.abs(xf @ to_f64(As[i]).T) @ np.abs(to_f64(Bs[i])).T) if r else np.zeros_like(S)
+        assert _oracle_bound_ok(got, ref, S, T, alpha / max(r, 1)) == 0, (i, N, K)
+
+
+def test_decode_split_fixup_counters_left_zero(qops):
+    """A call whose K is split across workgroups leaves the workspace's arrival
+    counters zero, so the same workspace serves any later call; repeated calls
+    through one workspace are bitwise identical."""
+    M, N, K, r = 16, 1000, 11008, 16
+    x = dev(synth.activations(M, K, 3500))
+    qw = gpu_quant(qops, synth.weight(N, K, 3501))
+    A, B = (dev(a) for a in synth.adapters(N, K, r, 3502, 3503))
+    ws = qops.Workspace("cuda")
+    assert qops.workspace_bytes(0, M, N, K, r) > 16384
+    y1 = qops.lora_fwd(x, qw, A, B, 32.0, ws=ws)
+    torch.cuda.synchronize()
+    assert int(ws.buf[:16384].view(torch.int32).abs().sum()) == 0
+    y2 = qops.lora_fwd(x, qw, A, B, 32.0, ws=ws)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
