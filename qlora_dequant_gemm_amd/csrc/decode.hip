@@ -218,7 +218,7 @@ __global__ __launch_bounds__(256, 2) void k_dec_fwd(DecFwdBatch bt, Codebook cb)
     constexpr bool kPre = decltype(pre)::value;
     const bool kvalid = ss * 4 + g < nbr;
     u32x4 afl[2];
-    if constexpr (RT > 2) load_adapter(ss, 0, afl);
+    if constexpr (RT > 0 && !kPrefetchA) load_adapter(ss, 0, afl);
     if constexpr (kPre) load(ss + 1, nxt);
 #pragma unroll
     for (int nt = 0; nt < kDecNT; ++nt) {
@@ -334,7 +334,12 @@ __global__ __launch_bounds__(256, 2) void k_dec_fwd(DecFwdBatch bt, Codebook cb)
     return;
   }
   // split K: partial sums [M][256] of this split, then the last split of the
-  // row block to arrive adds all of them in split order
+  // row block to arrive adds all of them in split order. The partials and the
+  // counter are written and read with device-scope atomic accesses, which are
+  // coherent across the XCDs' L2 caches without writing back or invalidating
+  // them (a device-scope fence would do both, for every workgroup); each wave
+  // waits for its partial stores to complete before the workgroup barrier that
+  // precedes the arrival increment.
   float* const part_rb = bt.part + (P.part0 + static_cast<int64_t>(b) * P.S) * (M * kDecRows);
   float* const mine = part_rb + static_cast<int64_t>(s) * (M * kDecRows);
 #pragma unroll
@@ -342,25 +347,29 @@ __global__ __launch_bounds__(256, 2) void k_dec_fwd(DecFwdBatch bt, Codebook cb)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int m = 4 * g + v;
-      if (m < M) mine[m * kDecRows + 64 * w + 16 * nt + c] = acc[nt][v];
+      if (m < M)
+        __hip_atomic_store(mine + m * kDecRows + 64 * w + 16 * nt + c, acc[nt][v], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);                  // this wave's stores have completed
   __syncthreads();
   if (t == 0) {
-    __threadfence();
-    const unsigned old = atomicAdd(bt.cnt + P.cnt0 + b, 1u);
+    const unsigned old = __hip_atomic_fetch_add(bt.cnt + P.cnt0 + b, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
     last_flag = old == static_cast<unsigned>(P.S - 1);
   }
   __syncthreads();
   if (!last_flag) return;
-  __threadfence();
   const int64_t n0 = static_cast<int64_t>(b) * kDecRows;
   for (int idx = t; idx < M * kDecRows; idx += 256) {
     const int m = idx / kDecRows, jn = idx - m * kDecRows;
     float sum = 0.f;
-    for (int sp = 0; sp < P.S; ++sp) sum += part_rb[sp * (M * kDecRows) + idx];
+    for (int sp = 0; sp < P.S; ++sp)
+      sum += __hip_atomic_load(part_rb + sp * (M * kDecRows) + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (n0 + jn < N) P.y[m * N + n0 + jn] = bf16_bits(sum);
   }
-  if (t == 0) bt.cnt[P.cnt0 + b] = 0u;            // left zero for the next call
+  if (t == 0) __hip_atomic_store(bt.cnt + P.cnt0 + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------

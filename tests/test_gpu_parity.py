@@ -366,8 +366,9 @@ TILED = ["7b_mlp_up", "7b_mlp_down", "65b_up", "65b_attn"]
 
 
 def _elementwise_ok(got, ref, S, T, scale):
+    """Number of outputs outside the bound (NaN and Inf count as outside)."""
     bound = ref.abs() * 2.0 ** -8 + S * 2.0 ** -12 + T * (scale * 2.0 ** -8) + 1e-6
-    bad = ((got - ref).abs() > bound).sum().item()
+    bad = (~((got - ref).abs() <= bound)).sum().item()
     return bad
 
 
@@ -741,8 +742,9 @@ def test_grouped_forward_7b_qkv(qops):
 # weight-row steps per slice).
 # ---------------------------------------------------------------------------
 def _oracle_bound_ok(got, ref, S, T, scale):
+    """Number of outputs outside the bound (NaN and Inf count as outside)."""
     bound = np.abs(ref) * 2.0 ** -8 + S * 2.0 ** -12 + T * (scale * 2.0 ** -8) + 1e-6
-    return int((np.abs(got - ref) > bound).sum())
+    return int((~(np.abs(got - ref) <= bound)).sum())
 
 
 def _oracle_weight(w):
