@@ -235,12 +235,19 @@ class StackWorkload:
             for j in range(len(self.lin)):
                 d = synth.stack_linear_device(l, j, self.M)
                 w = d.pop("w")
+                N, K = w.shape
+                nb = N * K // 64
+                packed = torch.empty(N * K // 2, dtype=torch.uint8, device="cuda")
+                absmax = torch.empty(nb, dtype=torch.float32, device="cuda")
+                q = torch.empty(nb, dtype=torch.int8, device="cuda")
+                st = torch.empty((nb + 255) // 256, dtype=torch.float32, device="cuda")
                 torch.cuda.synchronize()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 with torch.cuda.stream(qstream):
                     e0.record(qstream)
-                    d["qw"] = ops.quantize_weight(w)
+                    ops.quantize_dq(w, packed=packed, absmax=absmax, q=q, step=st)
                     e1.record(qstream)
+                d["qw"] = ops.NF4Weight(packed, q, st, (N, K))
                 qev.append((e0, e1, w.numel()))
                 torch.cuda.synchronize()
                 del w

@@ -105,31 +105,39 @@ __device__ __forceinline__ u32x4 perm8(const u32x4& v) {
 constexpr int kDecNT = 4;                         // 16-row MFMA tiles per wave
 constexpr int kDecBufWord3 = 0x00020000;          // raw buffer descriptor word 3 on gfx9-family parts
 constexpr int kDecRows = 16 * kDecNT * 4;         // weight rows per item (four waves)
+constexpr int64_t kDecMaxSps = 8;               // 256-deep super-steps per item at most
 
 __device__ __forceinline__ int dec_item_of(int wg, int grid) {
   // grid is a multiple of 8: XCD (wg % 8) gets items [xcd * grid/8, ...)
   return (wg & 7) * (grid >> 3) + (wg >> 3);
 }
 
-// RT: rank tiles of 16 the kernel computes (0: no adapter; else a power of two
-// with 16 RT >= r). For r <= 16 the adapter rows travel with the stage.
-template <int RT>
-struct DecStage {
-  static constexpr int kPF = 1;
-  u32x4 cw[kDecNT][2];   // codes: the lane's block of each tile's weight row
-  u32x4 xa[8];           // 64 activations of x row c (natural order, then permuted)
-  u32x4 af[kPF][2];      // adapter rows for this wave's two MFMAs of t
-  float d[kDecNT];
-  int8_t q[kDecNT];
-};
+// LDS staging of one 256-deep super-step, shared by the workgroup's four waves:
+// 16 rows of x (rows past M zero) and, for ranks up to 16, the 16 adapter
+// rows, each row 32 chunks of 16 bytes with chunk k of row q at position
+// k ^ (q & 15) -- the 16 lanes of a read phase (rows c = 0..15, one logical
+// chunk) then touch 16 distinct bank groups.
+constexpr int kDecStageChunks = 2 * 16 * 32;      // x part, then adapter part
+__device__ __forceinline__ int dec_slot(int row, int chunk) { return row * 32 + (chunk ^ (row & 15)); }
 
-template <int RT>
+// RT: rank tiles of 16 the kernel computes (0: no adapter; else a power of two
+// with 16 RT >= r). kQuad: every K of the launch is a multiple of 256.
+template <int RT, bool kQuad>
 __global__ __launch_bounds__(256, 2) void k_dec_fwd(DecFwdBatch bt, Codebook cb) {
   constexpr int kRT = RT > 0 ? RT : 1;
   constexpr int kRS = RT > 1 ? RT / 2 : 1;      // 32-deep rank chunks of the up-projection
-  constexpr bool kPrefetchA = RT == 1;
-  __shared__ float tsh[RT > 0 ? 4 * 16 * (16 * kRT + 4) : 1];
+  constexpr bool kStageA = RT == 1;             // adapter rows staged in LDS with x
+  // two stages of x (+ adapter), and for kQuad the item's scale codes and
+  // steps per (row, super-step); after the main loop the same memory holds
+  // the four waves' parts of t
+  __shared__ u32x4 stg0[kDecStageChunks], stg1[kDecStageChunks];
+  __shared__ uint32_t lq[kQuad ? kDecRows * kDecMaxSps : 1];
+  __shared__ float ld[kQuad ? kDecRows * kDecMaxSps : 1];
   __shared__ int last_flag;
+  float* const tsh = reinterpret_cast<float*>(stg0);
+
+  // workgroup barrier that orders the compiler's LDS accesses too
+  auto sync = [&] { lds_barrier_on(stg0, stg1, lq, ld); };
 
   const int item = dec_item_of(blockIdx.x, gridDim.x);
   if (item >= bt.items) return;
@@ -143,66 +151,72 @@ __global__ __launch_bounds__(256, 2) void k_dec_fwd(DecFwdBatch bt, Codebook cb)
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int g = lane >> 4, c = lane & 15;
   const int M = bt.M, r = bt.r;
-  const int64_t N = P.N, K = P.K;
-  const int64_t nbr = K / 64, nss = cdiv(nbr, 4);
+  // sizes fit 32 bits (N, K <= 2^21): only the base addresses are 64-bit
+  const int N = P.N, K = P.K;
+  const int nbr = K / 64, nss = (nbr + 3) / 4;
   const int local = item - P.item0;
   const int b = local / P.S, s = local - (local / P.S) * P.S;
-  const int64_t ss0 = static_cast<int64_t>(s) * P.sps;
-  const int64_t ss1 = imin(ss0 + P.sps, nss);
-  const int64_t nb0 = static_cast<int64_t>(b) * kDecRows + 64 * w;   // this wave's first row
+  const int ss0 = s * P.sps;
+  const int ss1 = ss0 + P.sps < nss ? ss0 + P.sps : nss;
+  const int nit = ss1 - ss0;
+  const int nb0 = b * kDecRows + 64 * w;                 // this wave's first row
 
-  // every load is unconditional (rows past N re-read row N - 1 and are never
-  // stored; x rows past M and adapter rows past r read as zero through the
-  // buffer descriptors' range checks), so the only branches of the loop are
-  // uniform loop control and the compiler can keep the next stage in flight
-  const uint8_t* prow[kDecNT];
-  int64_t bix[kDecNT];
-#pragma unroll
-  for (int nt = 0; nt < kDecNT; ++nt) {
-    const int64_t n = imin(nb0 + 16 * nt + c, N - 1);
-    prow[nt] = P.packed + n * (K / 2);
-    bix[nt] = n * nbr;
-  }
+  // Every operand is read through a buffer descriptor whose range check
+  // returns zero outside it: the wave's 64 weight rows, their scale codes and
+  // steps (rows past N read as zero codes with a zero scale), x (rows past M),
+  // the adapter (rows past r). Values that are wave-uniform by construction go
+  // through readfirstlane so that the descriptors live in scalar registers.
+  const int rows_valid = __builtin_amdgcn_readfirstlane(N - nb0 < 0 ? 0 : (N - nb0 < 64 ? N - nb0 : 64));
+  const int nbw = __builtin_amdgcn_readfirstlane(nb0 < N ? nb0 : 0);
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(P.packed + static_cast<int64_t>(nbw) * (K / 2)), 0, rows_valid * (K / 2), kDecBufWord3);
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(P.x), 0, static_cast<int>(M * K * 2), kDecBufWord3);
-  const uint32_t xoff = static_cast<uint32_t>(c * K * 2);
+      const_cast<uint16_t*>(P.x), 0, M * K * 2, kDecBufWord3);
   const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(RT > 0 ? P.A : P.x), 0, static_cast<int>(RT > 0 ? r * K * 2 : 0), kDecBufWord3);
+      const_cast<uint16_t*>(RT > 0 ? P.A : P.x), 0, RT > 0 ? r * K * 2 : 0, kDecBufWord3);
 
-  // adapter rows 16 jt + c of block 4 ss + g, 8-element pieces 2w and 2w + 1
-  // (wave w computes those two MFMAs of t; past K they read as zero)
-  auto load_adapter = [&](int64_t ss, int jt, u32x4 (&af)[2]) {
-    const int64_t kbr = ss * 4 + g;
-    const int64_t kb = imin(kbr, nbr - 1);
-    const uint32_t off = kbr < nbr ? static_cast<uint32_t>(((16 * jt + c) * K + kb * 64 + 16 * w) * 2) : 0x80000000u;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      af[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ars, off + 16 * i, 0, 0));
+  // The super-steps of the item in an order rotated per workgroup, so that
+  // the workgroups resident at one time read different 128-byte columns of
+  // their rows (the sum over K does not depend on the order).
+  const int rot = nit > 0 ? (b * 5) % nit : 0;
+  auto ss_of = [&](int i) {
+    const int j = i + rot;
+    return ss0 + (j >= nit ? j - nit : j);
   };
-  // activations first: the end of the previous super-step waits for them
-  // (and permutes them in place) while the codes stay in flight
-  auto load = [&](int64_t ss, DecStage<RT>& st) {
-    const int64_t kb = imin(ss * 4 + g, nbr - 1);
-    const uint32_t xo = xoff + static_cast<uint32_t>(kb * 128);
+
+  // scale codes and steps of this lane's rows (kQuad: one aligned word of four
+  // codes and one step per row and super-step, kept in LDS for the item; else
+  // loaded with the codes)
+  const int64_t blk0w = static_cast<int64_t>(nbw) * nbr;
+  const int sb0w = __builtin_amdgcn_readfirstlane(static_cast<int>(blk0w & 255));
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(P.qscale + blk0w), 0, rows_valid * nbr, kDecBufWord3);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(P.step + (blk0w >> 8)), 0, ((sb0w + rows_valid * nbr + 255) >> 8) * 4, kDecBufWord3);
+  // stage DMA: wave w moves chunks [256 w, 256 w + 256) of the stage, four
+  // instructions of 64 lanes; lane l of instruction h lands at slot
+  // 256 w + 64 h + l, i.e. row q = slot / 32 (x rows 0-15, then adapter rows),
+  // physical chunk slot % 32, and fetches logical chunk phys ^ (q & 15)
+  uint32_t doff[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      st.xa[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, xo + 16 * j, 0, 0));
+  for (int h = 0; h < 4; ++h) {
+    const int slot = 256 * w + 64 * h + lane;
+    const int q = (slot >> 5) & 15, phys = slot & 31;
+    doff[h] = static_cast<uint32_t>(q * K * 2 + ((phys ^ q) * 16));
+  }
+  auto dma_stage = [&](int ss, u32x4* stg) {
+    const uint32_t so = static_cast<uint32_t>(ss * 512);
 #pragma unroll
-    for (int nt = 0; nt < kDecNT; ++nt) {
-      st.cw[nt][0] = ld16(prow[nt] + kb * 32);
-      st.cw[nt][1] = ld16(prow[nt] + kb * 32 + 16);
-      st.q[nt] = P.qscale[bix[nt] + kb];
-      st.d[nt] = P.step[(bix[nt] + kb) >> 8];
+    for (int h = 0; h < 4; ++h) {
+      lds_void* dst = (lds_void*)(stg + 256 * w + 64 * h);
+      if (w < 2)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, dst, 16, doff[h], so, 0, 0);
+      else if (kStageA)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, dst, 16, doff[h], so, 0, 0);
     }
-    if constexpr (kPrefetchA) {
-#pragma unroll
-      for (int jt = 0; jt < RT; ++jt) load_adapter(ss, jt, st.af[jt]);
-    }
   };
-  auto permute_x = [&](DecStage<RT>& st) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) st.xa[j] = perm8(st.xa[j]);
-  };
+  // wave-uniform number of stage-DMA instructions this wave issues
+  const int ndma = (w < 2 || kStageA) ? 4 : 0;
 
   f32x4 acc[kDecNT], tacc[kRT];
 #pragma unroll
@@ -210,71 +224,161 @@ __global__ __launch_bounds__(256, 2) void k_dec_fwd(DecFwdBatch bt, Codebook cb)
 #pragma unroll
   for (int jt = 0; jt < kRT; ++jt) tacc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // one super-step on `cur`; with kPre the next one is requested into `nxt`
-  // first (and its activations permuted at the end). Larger ranks request
-  // their adapter rows before the next stage, so that waiting for them leaves
-  // the stage in flight.
-  auto body = [&](auto pre, int64_t ss, const DecStage<RT>& cur, DecStage<RT>& nxt) {
-    constexpr bool kPre = decltype(pre)::value;
-    const bool kvalid = ss * 4 + g < nbr;
-    u32x4 afl[2];
-    if constexpr (RT > 0 && !kPrefetchA) load_adapter(ss, 0, afl);
-    if constexpr (kPre) load(ss + 1, nxt);
+  // codes (and for ragged K the scale codes and steps) of super-step ss,
+  // requested one super-step ahead into registers
+  struct Codes {
+    u32x4 cw[kDecNT][2];
+    float d[kQuad ? 1 : kDecNT];
+    uint32_t q[kQuad ? 1 : kDecNT];
+  };
+  auto load_codes = [&](int ss, Codes& C) {
+    const int kbr = ss * 4 + g;
+    const int kb = kbr < nbr ? kbr : nbr - 1;
 #pragma unroll
     for (int nt = 0; nt < kDecNT; ++nt) {
-      const float sc = kvalid ? block_scale(cur.q[nt], cur.d[nt]) : 0.0f;
+      const int row = 16 * nt + c;
+      const uint32_t co = static_cast<uint32_t>(row * (K / 2) + kb * 32);
+      C.cw[nt][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(crs, co, 0, 0));
+      C.cw[nt][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(crs, co + 16, 0, 0));
+      if constexpr (!kQuad) {
+        const int bl = row * nbr + kb;
+        C.q[nt] = __builtin_amdgcn_raw_buffer_load_b8(qrs, static_cast<uint32_t>(bl), 0, 0);
+        C.d[nt] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(srs, static_cast<uint32_t>(((sb0w + bl) >> 8) * 4), 0, 0));
+      }
+    }
+  };
+  // adapter rows 16 jt + c of block kb, pieces 2w and 2w + 1, straight from
+  // memory (ranks past 16; lanes past K read zero)
+  auto load_adapter = [&](int ss, int jt, u32x4 (&a)[2]) {
+    const int kbr = ss * 4 + g;
+    const int kb = kbr < nbr ? kbr : nbr - 1;
+    const uint32_t o = static_cast<uint32_t>(((16 * jt + c) * K + kb * 64 + 16 * w) * 2);
+    const uint32_t off = kbr < nbr ? o : 0x80000000u;
+    a[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ars, off, 0, 0));
+    a[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ars, off + 16, 0, 0));
+  };
+
+  Codes c0, c1;
+  if constexpr (kQuad) {
+    // thread t owns row 64 w + lane of the workgroup's 256 rows
+    uint32_t qv[kDecMaxSps];
+    float dv[kDecMaxSps];
+#pragma unroll
+    for (int u = 0; u < kDecMaxSps; ++u) {
+      const int bl = lane * nbr + (ss0 + u) * 4;
+      const bool in = u < nit;
+      qv[u] = in ? __builtin_amdgcn_raw_buffer_load_b32(qrs, static_cast<uint32_t>(bl), 0, 0) : 0u;
+      dv[u] = in ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                       srs, static_cast<uint32_t>(((sb0w + bl) >> 8) * 4), 0, 0))
+                 : 0.0f;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (nit > 0) {                                 // the first stage goes out behind them
+      load_codes(ss_of(0), c0);
+      dma_stage(ss_of(0), stg0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kDecMaxSps; ++u) {
+      lq[t * kDecMaxSps + u] = qv[u];
+      ld[t * kDecMaxSps + u] = dv[u];
+    }
+    sync();
+  } else if (nit > 0) {
+    load_codes(ss_of(0), c0);
+    dma_stage(ss_of(0), stg0);
+  }
+
+
+  // iteration i: (1) every wave is past its reads of the stage buffer about to
+  // be refilled (barrier); (2) request the codes and the stage of the next
+  // super-step; (3) wait until this wave's part of the current stage has
+  // landed, then for all waves' parts (barrier); (4) decode and multiply.
+  // The waits are explicit: the compiler does not track LDS written by DMA.
+  auto iter = [&](auto pre, int i, const Codes& cur, Codes& nxt, const u32x4* stg, u32x4* stg_next) {
+    constexpr bool kPre = decltype(pre)::value;
+    const int ss = ss_of(i);
+    // the lane's k-block is past K only in the ragged last super-step
+    const bool kvalid = kQuad || ss * 4 + g < nbr;
+    const uint32_t lv = kvalid ? 0xFFFFFFFFu : 0u;
+    const u32x4 live = {lv, lv, lv, lv};
+    sync();
+    if constexpr (kPre) {
+      load_codes(ss_of(i + 1), nxt);
+      dma_stage(ss_of(i + 1), stg_next);
+      __builtin_amdgcn_sched_barrier(0);
+      // outstanding, oldest first: [codes i, stage i] [codes i+1, stage i+1]
+      if (ndma) wait_vm<2 * kDecNT + 4 + (kQuad ? 0 : 2 * kDecNT)>();
+      else wait_vm<2 * kDecNT + (kQuad ? 0 : 2 * kDecNT)>();
+    } else {
+      wait_vm<0>();
+    }
+    sync();
+    // past K the staged rows hold the next row's values: the lane's
+    // activations (and adapter values) are masked to zero there
+    u32x4 xa[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xa[j] = perm8(stg[dec_slot(c, 8 * g + j)]) & live;
+#pragma unroll
+    for (int nt = 0; nt < kDecNT; ++nt) {
+      float sc;
+      if constexpr (kQuad) {
+        const int row = 64 * w + 16 * nt + c;
+        const int8_t qc = static_cast<int8_t>(lq[row * kDecMaxSps + (ss - ss0)] >> (8 * g));
+        sc = block_scale(qc, ld[row * kDecMaxSps + (ss - ss0)]);
+      } else {
+        sc = kvalid ? block_scale(static_cast<int8_t>(cur.q[nt]), cur.d[nt]) : 0.0f;
+      }
       const PermTable tb = make_ptable(cb, sc);
       const uint32_t pw[8] = {cur.cw[nt][0].x, cur.cw[nt][0].y, cur.cw[nt][0].z, cur.cw[nt][0].w,
                               cur.cw[nt][1].x, cur.cw[nt][1].y, cur.cw[nt][1].z, cur.cw[nt][1].w};
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        acc[nt] = mfma16(as_bf16x8(cur.xa[j]), as_bf16x8(decode8_perm(pw[j], tb)), acc[nt]);
+        acc[nt] = mfma16(as_bf16x8(xa[j]), as_bf16x8(decode8_perm(pw[j], tb)), acc[nt]);
     }
     if constexpr (RT > 0) {
       // pieces 2w, 2w + 1 of the lane's 64 activations (wave-uniform index)
-      const u32x4 x0 = w == 0 ? cur.xa[0] : w == 1 ? cur.xa[2] : w == 2 ? cur.xa[4] : cur.xa[6];
-      const u32x4 x1 = w == 0 ? cur.xa[1] : w == 1 ? cur.xa[3] : w == 2 ? cur.xa[5] : cur.xa[7];
-      if constexpr (kPrefetchA) {
-#pragma unroll
-        for (int jt = 0; jt < RT; ++jt) {
-          tacc[jt] = mfma16(as_bf16x8(x0), as_bf16x8(perm8(cur.af[jt][0])), tacc[jt]);
-          tacc[jt] = mfma16(as_bf16x8(x1), as_bf16x8(perm8(cur.af[jt][1])), tacc[jt]);
-        }
+      const u32x4 x0 = w == 0 ? xa[0] : w == 1 ? xa[2] : w == 2 ? xa[4] : xa[6];
+      const u32x4 x1 = w == 0 ? xa[1] : w == 1 ? xa[3] : w == 2 ? xa[5] : xa[7];
+      if constexpr (kStageA) {
+        const u32x4 a0 = stg[16 * 32 + dec_slot(c, 8 * g + 2 * w)] & live;
+        const u32x4 a1 = stg[16 * 32 + dec_slot(c, 8 * g + 2 * w + 1)] & live;
+        tacc[0] = mfma16(as_bf16x8(x0), as_bf16x8(perm8(a0)), tacc[0]);
+        tacc[0] = mfma16(as_bf16x8(x1), as_bf16x8(perm8(a1)), tacc[0]);
       } else {
 #pragma unroll
         for (int jt = 0; jt < kRT; ++jt) {
-          if (jt > 0) load_adapter(ss, jt, afl);
-          tacc[jt] = mfma16(as_bf16x8(x0), as_bf16x8(perm8(afl[0])), tacc[jt]);
-          tacc[jt] = mfma16(as_bf16x8(x1), as_bf16x8(perm8(afl[1])), tacc[jt]);
+          u32x4 a[2];
+          load_adapter(ss, jt, a);
+          tacc[jt] = mfma16(as_bf16x8(x0), as_bf16x8(perm8(a[0])), tacc[jt]);
+          tacc[jt] = mfma16(as_bf16x8(x1), as_bf16x8(perm8(a[1])), tacc[jt]);
         }
       }
     }
-    if constexpr (kPre) permute_x(nxt);
   };
 
   using Pre = std::integral_constant<bool, true>;
   using NoPre = std::integral_constant<bool, false>;
-  DecStage<RT> st0, st1;
-  if (ss0 < ss1) {
-    load(ss0, st0);
-    permute_x(st0);
+  int i = 0;
+  for (; i + 2 < nit; i += 2) {
+    iter(Pre{}, i, c0, c1, stg0, stg1);
+    iter(Pre{}, i + 1, c1, c0, stg1, stg0);
   }
-  int64_t ss = ss0;
-  for (; ss + 2 < ss1; ss += 2) {
-    body(Pre{}, ss, st0, st1);
-    body(Pre{}, ss + 1, st1, st0);
+  if (i + 1 < nit) {
+    iter(Pre{}, i, c0, c1, stg0, stg1);
+    iter(NoPre{}, i + 1, c1, c0, stg1, stg0);
+  } else if (i < nit) {
+    iter(NoPre{}, i, c0, c1, stg0, stg1);
   }
-  if (ss + 1 < ss1) {
-    body(Pre{}, ss, st0, st1);
-    body(NoPre{}, ss + 1, st1, st0);
-  } else if (ss < ss1) {
-    body(NoPre{}, ss, st0, st1);
-  }
+  sync();                                  // the stage buffers become the t exchange
 
   // LoRA: sum the four waves' parts of t (fixed order), then add
   // scale * (t_hi + t_lo) . B^T to each tile
   if (RT > 0) {
-    constexpr int kLd = 16 * kRT + 4;
+    // rows padded against bank conflicts where the 64 rows still fit in the stage buffers
+    constexpr int kLd = 16 * kRT + (kRT < 8 ? 4 : 0);
+    static_assert(4 * 16 * kLd * 4 <= sizeof(u32x4) * 2 * kDecStageChunks, "t exchange exceeds the stage buffers");
     u32x4 bop[kDecNT][kRS];
 #pragma unroll
     for (int nt = 0; nt < kDecNT; ++nt) {
@@ -361,13 +465,29 @@ __global__ __launch_bounds__(256, 2) void k_dec_fwd(DecFwdBatch bt, Codebook cb)
   }
   __syncthreads();
   if (!last_flag) return;
+  // thread t adds 4 consecutive outputs over the splits, eight splits' loads
+  // in flight at a time; loads with the device-coherence bit (sc1) read what
+  // other XCDs wrote
+  const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+      part_rb, 0, static_cast<int>(P.S * M * kDecRows * 4), kDecBufWord3);
   const int64_t n0 = static_cast<int64_t>(b) * kDecRows;
-  for (int idx = t; idx < M * kDecRows; idx += 256) {
-    const int m = idx / kDecRows, jn = idx - m * kDecRows;
-    float sum = 0.f;
-    for (int sp = 0; sp < P.S; ++sp)
-      sum += __hip_atomic_load(part_rb + sp * (M * kDecRows) + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (n0 + jn < N) P.y[m * N + n0 + jn] = bf16_bits(sum);
+  for (int i4 = t; i4 < M * kDecRows / 4; i4 += 256) {
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    for (int sp0 = 0; sp0 < P.S; sp0 += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t off = static_cast<uint32_t>(((sp0 + u) * M * kDecRows + 4 * i4) * 4);
+        v[u] = sp0 + u < P.S ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, 16))
+                             : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sum += v[u];
+    }
+    const int m = 4 * i4 / kDecRows, jn = 4 * i4 - m * kDecRows;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (n0 + jn + e < N) P.y[m * N + n0 + jn + e] = bf16_bits(sum[e]);
   }
   if (t == 0) __hip_atomic_store(bt.cnt + P.cnt0 + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -395,6 +515,7 @@ DecPlan dec_plan(int64_t M, int G, const int64_t* N, const int64_t* K) {
       int64_t S = s_all < nss ? s_all : nss;
       int64_t sps = cdiv(nss, S);
       if (sps < min_sps) sps = min_sps < nss ? min_sps : nss;
+      if (sps > kDecMaxSps) sps = kDecMaxSps;   // bounded items balance the chip's load
       S = cdiv(nss, sps);
       const int64_t rb = cdiv(N[c0 + i], kDecRows);
       pl.S[c0 + i] = static_cast<int>(S);
@@ -461,8 +582,14 @@ hipError_t launch_dec_fwd(int64_t M, int G, const uint16_t* const* x, const int6
       }
     }
     bt.items = items;
+    bool quad = true;
+    for (int i = 0; i < cn; ++i) quad = quad && K[c0 + i] % 256 == 0;
     const dim3 grid(static_cast<unsigned>(round_up(items, 8)));
-#define QNF4_DEC(RTV) hipLaunchKernelGGL(k_dec_fwd<RTV>, grid, dim3(256), 0, stream, bt, cb)
+#define QNF4_DEC(RTV)                                                                    \
+  if (quad)                                                                              \
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(k_dec_fwd<RTV, true>), grid, dim3(256), 0, stream, bt, cb); \
+  else                                                                                   \
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(k_dec_fwd<RTV, false>), grid, dim3(256), 0, stream, bt, cb)
     switch (RT) {
       case 0: QNF4_DEC(0); break;
       case 1: QNF4_DEC(1); break;

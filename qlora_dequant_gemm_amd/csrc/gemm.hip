@@ -83,16 +83,7 @@ __device__ __forceinline__ int a_slot(int row, int ch) { return row * 8 + (ch ^ 
 // MFMA sub-step s uses k = 32h + 8s + (0..7) on both operands (the sum over k
 // is order-free), so a lane's codes for a step are one 16-byte word.
 // ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void gbl_void;
 constexpr int kBufferDword3 = 0x00020000;    // raw buffer descriptor word 3 on gfx9-family parts
-
-// Workgroup barrier without the fence of __syncthreads (whose release half
-// waits for every outstanding vector load). The asm memory clobber keeps the
-// compiler from moving memory accesses across it; the caller waits for the
-// LDS DMA it needs published, and its own LDS reads of the buffer about to be
-// refilled have all been consumed by then.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 struct BScale {
   float d[2];      // second-level steps of this lane's weight rows (N-blocks j)
@@ -104,13 +95,6 @@ struct BScale4 {   // the same for the four steps of a super-step
   uint32_t q[2];   // byte u = scale code of step 4S + u
 };
 
-// s_waitcnt vmcnt(n) with expcnt/lgkmcnt left alone (gfx9 encoding: vmcnt
-// bits 3:0 and 15:14), as the builtin so that the compiler's own wait
-// insertion knows which loads have completed
-constexpr int vmcnt_imm(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }
-template <int N>
-__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(N)); }
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // kQuad: K is a multiple of 256, so the four block-scale codes of a
 // super-step are one aligned 4-byte word of qscale and share one second-level

@@ -40,4 +40,32 @@ __device__ __forceinline__ s16x4 ds_read_tr(const u32x4* base, int elem_off) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Workgroup barrier without the fence of __syncthreads (whose release half
+// waits for every outstanding vector load). The asm memory clobber keeps the
+// compiler from moving memory accesses across it; the caller waits for the
+// LDS DMA it needs published, and its own LDS reads of the buffer about to be
+// refilled have all been consumed by then.
+// Workgroup barrier without a fence: the wait for global loads in flight that
+// __syncthreads' fence implies is left out (prefetches stay in flight across
+// it); the caller waits for its own LDS writes and buffer-to-LDS loads first.
+// The compiler sees the asm as touching memory, but may still move accesses
+// to a __shared__ array whose address never escapes across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// The same after this wave's LDS operations are done, with the kernel's
+// __shared__ arrays named as operands, so that no access to them moves across.
+template <typename A, typename B, typename C, typename D>
+__device__ __forceinline__ void lds_barrier_on(A* a, B* b, C* c, D* d) {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::"s"(a), "s"(b), "s"(c), "s"(d) : "memory");
+}
+
+// s_waitcnt vmcnt(n) with expcnt/lgkmcnt left alone (gfx9 encoding: vmcnt
+// bits 3:0 and 15:14), as the builtin so that the compiler's own wait
+// insertion knows which loads have completed
+constexpr int vmcnt_imm(int n) { return ((n >> 4) << 14) | 0x0F70 | (n & 15); }
+template <int N>
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(N)); }
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 }  // namespace qnf4
