@@ -63,7 +63,8 @@ typedef enum {
   QLORA_ERR_WORKSPACE = 5, /* workspace missing or smaller than required */
   QLORA_ERR_DTYPE = 6,     /* unknown input dtype */
   QLORA_ERR_HIP = 7,       /* a HIP call failed; see qlora_last_hip_error() */
-  QLORA_ERR_INIT = 8       /* the codebook could not be derived */
+  QLORA_ERR_INIT = 8,      /* the codebook could not be derived */
+  QLORA_ERR_SCRATCH = 9    /* sizes need more than QLORA_NOALLOC_SCRATCH_BYTES */
 } qlora_status;
 
 typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
@@ -165,6 +166,32 @@ int qlora_nf4_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K,
                        const float* step, const uint16_t* A, const uint16_t* B,
                        int r, float alpha, uint16_t* y, void* workspace,
                        size_t ws_bytes, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the forward
+ * of qlora_nf4_lora_fwd, same arguments, results and limits, but without a
+ * workspace argument. The split partial sums and arrival counters live in a
+ * scratch array built into the library, QLORA_NOALLOC_SCRATCH_BYTES per GPU,
+ * held from the first call on that GPU until the process ends; the call
+ * allocates nothing (no hipMalloc or hipFree, no host heap).
+ *   Sizes whose workspace, qlora_workspace_bytes(0, M, N, K, r), exceeds
+ *   QLORA_NOALLOC_SCRATCH_BYTES return QLORA_ERR_SCRATCH before any launch
+ *   (the 4096 x 4096 to 22016 x 8192 layers fit at every M up to 16384 and
+ *   every rank; very long K at M <= 16, or M in the hundreds of thousands,
+ *   does not).
+ *   Every call on one GPU shares that GPU's scratch: calls that overlap in
+ *   time on one GPU (different streams or threads without ordering between
+ *   them) race and give wrong results; order them on one stream. Each call
+ *   first clears the counters (a small kernel on `stream`, so a captured call
+ *   clears them on every replay), then runs the forward kernels.
+ */
+#define QLORA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int qlora_nf4_lora_fwd_noalloc(const uint16_t* x, int64_t M, int64_t N,
+                               int64_t K, const uint8_t* packed,
+                               const int8_t* qscale, const float* step,
+                               const uint16_t* A, const uint16_t* B, int r,
+                               float alpha, uint16_t* y, void* stream);
 
 /*
  * Forward of several QLoRA linears that share their input (e.g. the q, k and

@@ -6,4 +6,4 @@ block constants, and the fused dequantize-to-bf16 matmuls of one QLoRA linear
 HIP kernels behind the C ABI declared in include/qlora_nf4.h.
 """
 from .ops import (NF4Weight, Workspace, bwd_dx, codebook, dequant, dq_scales,  # noqa: F401
-                  lora_fwd, quantize, quantize_dq, quantize_weight, workspace_bytes)
+                  lora_fwd, lora_fwd_noalloc, quantize, quantize_dq, quantize_weight, workspace_bytes)

@@ -12,7 +12,8 @@ LIB_PATH = os.path.join(HERE, "libqlora_nf4.so")
 QLORA_OK = 0
 STATUS = {0: "QLORA_OK", 1: "QLORA_ERR_NULL", 2: "QLORA_ERR_SHAPE", 3: "QLORA_ERR_ALIGN",
           4: "QLORA_ERR_RANK", 5: "QLORA_ERR_WORKSPACE", 6: "QLORA_ERR_DTYPE",
-          7: "QLORA_ERR_HIP", 8: "QLORA_ERR_INIT"}
+          7: "QLORA_ERR_HIP", 8: "QLORA_ERR_INIT", 9: "QLORA_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 32 << 20
 F32, BF16 = 0, 1
 
 # (name, restype, argtypes) for every symbol the header declares.
@@ -25,6 +26,8 @@ SIGNATURES = [
     ("qlora_workspace_bytes", _sz, [_i32, _i64, _i64, _i64, _i32]),
     ("qlora_nf4_lora_fwd", _i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _f32,
                                   _vp, _vp, _sz, _vp]),
+    ("qlora_nf4_lora_fwd_noalloc", _i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _f32,
+                                          _vp, _vp]),
     ("qlora_nf4_lora_fwd_grouped", _i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32,
                                           _vp, _vp, _sz, _vp]),
     ("qlora_nf4_lora_fwd_batched", _i32, [_i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32,

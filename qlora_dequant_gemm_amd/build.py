@@ -17,7 +17,8 @@ LIB = os.path.join(HERE, "libqlora_nf4.so")
 OBJ = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["codebook.cpp", "api.cpp", "quant.hip", "lora.hip", "small.hip", "decode.hip", "gemm.hip", "grad.hip", "merge.hip"]
+SOURCES = ["codebook.cpp", "api.cpp", "quant.hip", "lora.hip", "small.hip", "decode.hip", "gemm.hip", "grad.hip", "merge.hip",
+           "noalloc.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

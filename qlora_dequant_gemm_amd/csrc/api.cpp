@@ -77,6 +77,7 @@ const char* qlora_status_string(int status) {
     case QLORA_ERR_DTYPE: return "unknown dtype";
     case QLORA_ERR_HIP: return "HIP error";
     case QLORA_ERR_INIT: return "codebook derivation failed";
+    case QLORA_ERR_SCRATCH: return "sizes need more than the built-in scratch of the allocation-free forward";
     default: return "unknown status";
   }
 }
@@ -154,6 +155,30 @@ int qlora_nf4_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K, const
   if (!cb) return QLORA_ERR_INIT;
   return hip_status(qnf4::launch_lora_fwd(x, M, N, K, packed, qscale, step, A, B, r, alpha, y, workspace, *cb,
                                           as_stream(stream)));
+}
+
+int qlora_nf4_lora_fwd_noalloc(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
+                               const int8_t* qscale, const float* step, const uint16_t* A, const uint16_t* B, int r,
+                               float alpha, uint16_t* y, void* stream) {
+  if (!x || !y) return QLORA_ERR_NULL;
+  int st = check_weight(packed, qscale, step);
+  if (st) return st;
+  st = check_mm(M, N, K);
+  if (st) return st;
+  st = check_adapter(A, B, r);
+  if (st) return st;
+  if (!aligned16(x) || !aligned16(y)) return QLORA_ERR_ALIGN;
+  const size_t need = qnf4::ws_layout(0, M, N, K, r).total;
+  if (need > qnf4::kNoAllocScratchBytes) return QLORA_ERR_SCRATCH;
+  const qnf4::Codebook* cb = qnf4::codebook();
+  if (!cb) return QLORA_ERR_INIT;
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = qnf4::noalloc_scratch(&ws, as_stream(stream));
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return hip_status(
+      qnf4::launch_lora_fwd(x, M, N, K, packed, qscale, step, A, B, r, alpha, y, ws, *cb, as_stream(stream)));
 }
 
 int qlora_nf4_lora_fwd_grouped(const uint16_t* x, int64_t M, int64_t K, int G, const uint8_t* const* packed,

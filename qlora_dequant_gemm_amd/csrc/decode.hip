@@ -495,67 +495,62 @@ __global__ __launch_bounds__(256, 2) void k_dec_fwd(DecFwdBatch bt, Codebook cb)
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-DecPlan dec_plan(int64_t M, int G, const int64_t* N, const int64_t* K) {
-  DecPlan pl;
-  pl.S.assign(G, 1);
-  pl.sps.assign(G, 1);
-  // chunks of at most kDecMaxProblems weights, one launch each; the plan of a
-  // chunk depends only on that chunk
-  for (int c0 = 0; c0 < G; c0 += kDecMaxProblems) {
-    const int cn = G - c0 < kDecMaxProblems ? G - c0 : kDecMaxProblems;
-    int64_t rb_total = 0;
-    for (int i = 0; i < cn; ++i) rb_total += cdiv(N[c0 + i], kDecRows);
-    // about kDecTargetItems items per launch; at M > 4 a split covers at least
-    // two super-steps (its fp32 partials are M KB per 256 rows)
-    const int64_t s_all = rb_total >= kDecTargetItems / 2 ? 1 : cdiv(kDecTargetItems, rb_total);
-    const int64_t min_sps = M > 4 ? 2 : 1;
-    int64_t items = 0, slots = 0, counters = 0;
-    for (int i = 0; i < cn; ++i) {
-      const int64_t nss = cdiv(K[c0 + i] / 64, 4);
-      int64_t S = s_all < nss ? s_all : nss;
-      int64_t sps = cdiv(nss, S);
-      if (sps < min_sps) sps = min_sps < nss ? min_sps : nss;
-      if (sps > kDecMaxSps) sps = kDecMaxSps;   // bounded items balance the chip's load
-      S = cdiv(nss, sps);
-      const int64_t rb = cdiv(N[c0 + i], kDecRows);
-      pl.S[c0 + i] = static_cast<int>(S);
-      pl.sps[c0 + i] = static_cast<int>(sps);
-      items += rb * S;
-      if (S > 1) {
-        slots += rb * S;
-        counters += rb;
-      }
+// The weights go in chunks of at most kDecMaxProblems, one launch each; the
+// plan of a chunk depends only on that chunk.
+DecChunkPlan dec_plan_chunk(int64_t M, int cn, const int64_t* N, const int64_t* K) {
+  DecChunkPlan pl;
+  int64_t rb_total = 0;
+  for (int i = 0; i < cn; ++i) rb_total += cdiv(N[i], kDecRows);
+  // about kDecTargetItems items per launch; at M > 4 a split covers at least
+  // two super-steps (its fp32 partials are M KB per 256 rows)
+  const int64_t s_all = rb_total >= kDecTargetItems / 2 ? 1 : cdiv(kDecTargetItems, rb_total);
+  const int64_t min_sps = M > 4 ? 2 : 1;
+  for (int i = 0; i < cn; ++i) {
+    const int64_t nss = cdiv(K[i] / 64, 4);
+    int64_t S = s_all < nss ? s_all : nss;
+    int64_t sps = cdiv(nss, S);
+    if (sps < min_sps) sps = min_sps < nss ? min_sps : nss;
+    if (sps > kDecMaxSps) sps = kDecMaxSps;     // bounded items balance the chip's load
+    S = cdiv(nss, sps);
+    const int64_t rb = cdiv(N[i], kDecRows);
+    pl.S[i] = static_cast<int>(S);
+    pl.sps[i] = static_cast<int>(sps);
+    pl.items += rb * S;
+    if (S > 1) {
+      pl.slots += rb * S;
+      pl.counters += rb;
     }
-    if (slots > pl.max_slots) pl.max_slots = slots;
-    if (counters > pl.max_counters) pl.max_counters = counters;
-    if (items > pl.max_items) pl.max_items = items;
   }
-  pl.part_bytes = align256(static_cast<size_t>(pl.max_slots * M * kDecRows * 4));
   return pl;
 }
 
 size_t dec_workspace_bytes(int64_t M, int G, const int64_t* N, const int64_t* K) {
-  const DecPlan pl = dec_plan(M, G, N, K);
-  if (pl.max_slots == 0) return 0;
-  return kWsCounterBytes + pl.part_bytes;
+  int64_t max_slots = 0;
+  for (int c0 = 0; c0 < G; c0 += kDecMaxProblems) {
+    const int cn = G - c0 < kDecMaxProblems ? G - c0 : kDecMaxProblems;
+    const DecChunkPlan pl = dec_plan_chunk(M, cn, N + c0, K + c0);
+    if (pl.slots > max_slots) max_slots = pl.slots;
+  }
+  if (max_slots == 0) return 0;
+  return kWsCounterBytes + align256(static_cast<size_t>(max_slots * M * kDecRows * 4));
 }
 
 hipError_t launch_dec_fwd(int64_t M, int G, const uint16_t* const* x, const int64_t* N, const int64_t* K,
                           const uint8_t* const* packed, const int8_t* const* qscale, const float* const* step,
                           const uint16_t* const* A, const uint16_t* const* B, int r, float alpha,
                           uint16_t* const* y, void* ws, const Codebook& cb, hipStream_t stream) {
-  const DecPlan pl = dec_plan(M, G, N, K);
   char* wsb = static_cast<char*>(ws);
   const int RT = r <= 0 ? 0 : r <= 16 ? 1 : r <= 32 ? 2 : r <= 64 ? 4 : 8;
   for (int c0 = 0; c0 < G; c0 += kDecMaxProblems) {
     const int cn = G - c0 < kDecMaxProblems ? G - c0 : kDecMaxProblems;
+    const DecChunkPlan pl = dec_plan_chunk(M, cn, N + c0, K + c0);
     DecFwdBatch bt{};
     bt.count = cn;
     bt.M = static_cast<int>(M);
     bt.r = r;
     bt.scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
-    bt.cnt = pl.max_slots ? reinterpret_cast<unsigned*>(wsb) : nullptr;
-    bt.part = pl.max_slots ? reinterpret_cast<float*>(wsb + kWsCounterBytes) : nullptr;
+    bt.cnt = pl.slots ? reinterpret_cast<unsigned*>(wsb) : nullptr;
+    bt.part = pl.slots ? reinterpret_cast<float*>(wsb + kWsCounterBytes) : nullptr;
     int items = 0, slot = 0, cnt = 0;
     for (int i = 0; i < cn; ++i) {
       const int q = c0 + i;
@@ -569,8 +564,8 @@ hipError_t launch_dec_fwd(int64_t M, int G, const uint16_t* const* x, const int6
       P.y = y[q];
       P.N = static_cast<int>(N[q]);
       P.K = static_cast<int>(K[q]);
-      P.S = pl.S[q];
-      P.sps = pl.sps[q];
+      P.S = pl.S[i];
+      P.sps = pl.sps[i];
       P.item0 = items;
       const int rb = static_cast<int>(cdiv(N[q], kDecRows));
       items += rb * P.S;

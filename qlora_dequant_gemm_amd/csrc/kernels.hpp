@@ -7,8 +7,6 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include <vector>
-
 #include "codebook.hpp"
 
 namespace qnf4 {
@@ -56,12 +54,13 @@ struct DecFwdBatch {
   float* part;              // [slots][M][256] fp32 partial sums
   unsigned* cnt;            // arrival counters, one per split row block
 };
-struct DecPlan {
-  std::vector<int> S, sps;
-  int64_t max_slots = 0, max_counters = 0, max_items = 0;
-  size_t part_bytes = 0;
+// Plan of one launch (at most kDecMaxProblems weights): splits of K per
+// weight, super-steps per split, and the workspace slots and counters used.
+struct DecChunkPlan {
+  int S[kDecMaxProblems], sps[kDecMaxProblems];
+  int64_t slots = 0, counters = 0, items = 0;
 };
-DecPlan dec_plan(int64_t M, int G, const int64_t* N, const int64_t* K);
+DecChunkPlan dec_plan_chunk(int64_t M, int cn, const int64_t* N, const int64_t* K);
 size_t dec_workspace_bytes(int64_t M, int G, const int64_t* N, const int64_t* K);
 // x[i], y[i] etc. are the G weights' operands (host arrays of device pointers)
 hipError_t launch_dec_fwd(int64_t M, int G, const uint16_t* const* x, const int64_t* N, const int64_t* K,
@@ -200,5 +199,12 @@ hipError_t launch_merge(const uint8_t* packed, const int8_t* qscale, const float
 hipError_t launch_lora_grad(const uint16_t* x, const uint16_t* dy, int64_t M, int64_t N, int64_t K,
                             const uint16_t* A, const uint16_t* B, int r, float alpha, float* dA, float* dB,
                             int accumulate, void* ws, hipStream_t stream);
+
+// Built-in scratch of the allocation-free forward: a file-scope device array
+// of kNoAllocScratchBytes per GPU. noalloc_scratch gives this device's address
+// of it (looked up once per device, on the first call with that device
+// current) after clearing its arrival counters on `stream`.
+constexpr size_t kNoAllocScratchBytes = size_t{32} << 20;
+hipError_t noalloc_scratch(void** ptr, hipStream_t stream);
 
 }  // namespace qnf4

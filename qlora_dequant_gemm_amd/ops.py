@@ -230,6 +230,25 @@ def lora_fwd(x, qw, A=None, B=None, alpha=0.0, out=None, ws=None):
     return out
 
 
+def lora_fwd_noalloc(x, qw, A=None, B=None, alpha=0.0, out=None):
+    """lora_fwd without a workspace: the library's built-in per-GPU scratch
+    holds the split partials (nothing is allocated when `out` is given)."""
+    N, K = qw.shape
+    M = _rows(x, "x")
+    _shape(x, (M, K), "x")
+    _adapter_rank(A, B, N, K)
+    if out is not None:
+        _shape(out, (M, N), "out")
+    _need(x, torch.bfloat16, "x")
+    _check_weight(qw, x.device)
+    r = _check_adapters(A, B, N, K, x.device)
+    out = _check_out(out, (M, N), x.device, "out")
+    _lib.check("qlora_nf4_lora_fwd_noalloc", _lib.lib().qlora_nf4_lora_fwd_noalloc(
+        _ptr(x), M, N, K, _ptr(qw.packed), _ptr(qw.qscale), _ptr(qw.step), _ptr(A), _ptr(B), r,
+        float(alpha), _ptr(out), _stream(x.device)))
+    return out
+
+
 def lora_fwd_grouped(x, qws, As=None, Bs=None, alpha=0.0, outs=None, ws=None):
     """The forward of several weights sharing x (one launch for M <= 16):
     returns [x . deq(W_i)^T + (alpha/r) . (x . A_i^T) . B_i^T for each i]."""

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 def test_abi_version_and_status_strings():
     L = _lib.lib()
     assert L.qlora_abi_version() == 1
-    for code in range(9):
+    for code in range(10):
         assert L.qlora_status_string(code)
     assert L.qlora_status_string(99) == b"unknown status"
 
@@ -143,6 +143,30 @@ def _bwd(dy=FAKE, M=16, N=64, K=64, packed=FAKE, q=FAKE, step=FAKE, A=V(0), B=V(
 ])
 def test_forward_rejects_bad_arguments(kwargs, status):
     assert _fwd(**kwargs) == status
+
+
+def _fwd_noalloc(x=FAKE, M=16, N=64, K=64, packed=FAKE, q=FAKE, step=FAKE, A=V(0), B=V(0), r=0, alpha=0.0,
+                 y=FAKE):
+    return _lib.lib().qlora_nf4_lora_fwd_noalloc(x, M, N, K, packed, q, step, A, B, r, alpha, y, V(0))
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(x=V(0)), 1), (dict(y=V(0)), 1), (dict(packed=V(0)), 1), (dict(step=V(0)), 1),
+    (dict(M=0), 2), (dict(K=96), 2), (dict(N=1 << 22), 2),
+    (dict(x=ODD), 3), (dict(y=ODD), 3),
+    (dict(r=8), 1), (dict(A=FAKE), 4), (dict(r=129, A=FAKE, B=FAKE), 4),
+    # a decode shape whose split partials need more than the built-in scratch,
+    # and a tiled one whose t = x . A^T does
+    (dict(M=16, N=4096, K=1 << 20), 9),
+    (dict(M=1 << 18, N=64, K=64, r=128, A=FAKE, B=FAKE), 9),
+])
+def test_noalloc_forward_rejects_before_any_launch(kwargs, status):
+    """Every rejection of the allocation-free forward happens on the host,
+    before the scratch is looked up or anything is launched."""
+    M, N, K = kwargs.get("M", 16), kwargs.get("N", 64), kwargs.get("K", 64)
+    if status == 9:
+        assert ops.workspace_bytes(0, M, N, K, kwargs.get("r", 0)) > _lib.NOALLOC_SCRATCH_BYTES
+    assert _fwd_noalloc(**kwargs) == status
 
 
 @pytest.mark.parametrize("kwargs,status", [
