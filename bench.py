@@ -524,10 +524,39 @@ def decode_walks(wl, stream, reps=10):
     return out
 
 
+def sclk_under_load(stream):
+    """The shader clock the driver reports while a burst of bf16 matmuls runs
+    (sysfs pp_dpm_sclk, the level marked current), or None where unreadable."""
+    import glob
+    import torch
+    paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    if not paths:
+        return None
+    a = torch.randn((8192, 8192), device="cuda").bfloat16()
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    seen = []
+    with torch.cuda.stream(stream):
+        for _ in range(200):
+            torch.matmul(a, a, out=b)
+    for _ in range(5):
+        time.sleep(0.02)
+        for p in paths:
+            try:
+                for line in open(p):
+                    if line.strip().endswith("*"):
+                        seen.append(int(line.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz")))
+            except (OSError, ValueError, IndexError):
+                pass
+    torch.cuda.synchronize()
+    return max(seen) if seen else None
+
+
 def context_figures(wl, stream):
     """Plain ROCm-library and streaming figures beside the fused kernels:
     torch.matmul (hipBLASLt) in bf16 on the dequantized weight at each
-    training shape, and a streaming read of the resident NF4 stack."""
+    training shape, plain streaming read and copy rates of HBM, and the shader
+    clock under load."""
     import torch
     ops = wl.ops
     out = {"bf16_gemm_on_dequantized_weight": {}}
@@ -548,14 +577,20 @@ def context_figures(wl, stream):
             "fwd_ms": round(mf, 4), "fwd_TFLOP/s": round(f / mf / 1e9, 1),
             "bwd_ms": round(mb, 4), "bwd_TFLOP/s": round(f / mb / 1e9, 1)}
         del wdq, yb, db
-    # streaming read: one float sum over every resident weight's packed codes
-    packs = [d["qw"].packed for row in wl.lay for d in row]
+    # plain streaming figures of the same HBM: one 2 GiB fp32 read (sum) and
+    # one 2 GiB device-to-device copy (bytes read + written), single launches
+    n = (2 << 30) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    c = torch.empty_like(a)
     tot = torch.zeros((), dtype=torch.float32, device="cuda")
-    views = [p.view(torch.float32) for p in packs]
-    ms = time_eager(lambda: [tot.add_(v.sum()) for v in views], stream, 5)
-    b = sum(p.numel() for p in packs)
-    out["stream_read_packed_stack"] = {"ms": round(ms, 4), "GB/s": round(b / ms / 1e6, 1), "bytes": b,
-                                       "how": "torch sum over each of the 224 packed code buffers"}
+    ms = time_eager(lambda: torch.sum(a, dim=0, out=tot), stream, 5)
+    out["stream_read_2GiB"] = {"ms": round(ms, 4), "GB/s": round(4 * n / ms / 1e6, 1), "bytes": 4 * n,
+                               "how": "torch.sum over a 2 GiB fp32 tensor"}
+    ms = time_eager(lambda: c.copy_(a), stream, 5)
+    out["copy_2GiB"] = {"ms": round(ms, 4), "GB/s": round(8 * n / ms / 1e6, 1), "bytes": 8 * n,
+                        "how": "torch copy_ of a 2 GiB fp32 tensor, bytes read + written"}
+    del a, c
+    out["sclk_mhz_under_load"] = sclk_under_load(stream)
     return out
 
 

@@ -42,7 +42,7 @@
 // (c < 8) is OR-ed into the high bytes, and the even and odd elements are paired
 // without interleaving: the word decodes to the element order
 // 0 2 4 6 1 3 5 7, and the activation fragments are permuted the same way
-// (a contraction does not depend on the order of its terms). About 19 VALU
+// (a contraction does not depend on the order of its terms). 17 VALU
 // operations per 8 weights.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -52,45 +52,6 @@
 #include "mm_common.hpp"
 
 namespace qnf4 {
-
-// entry j (0..7) = bf16(L[15 - j] * s): the magnitudes, largest first; low and
-// high bytes in separate planes of two dwords each
-struct PermTable {
-  uint32_t lo0, lo1, hi0, hi1;
-};
-
-__device__ __forceinline__ PermTable make_ptable(const Codebook& cb, float s) {
-  const uint32_t p0 = pack_bf16x2(cb.L[15] * s, cb.L[14] * s);
-  const uint32_t p1 = pack_bf16x2(cb.L[13] * s, cb.L[12] * s);
-  const uint32_t p2 = pack_bf16x2(cb.L[11] * s, cb.L[10] * s);
-  const uint32_t p3 = pack_bf16x2(cb.L[9] * s, cb.L[8] * s);
-  PermTable t;
-  t.lo0 = perm(p1, p0, 0x06040200u);
-  t.hi0 = perm(p1, p0, 0x07050301u);
-  t.lo1 = perm(p3, p2, 0x06040200u);
-  t.hi1 = perm(p3, p2, 0x07050301u);
-  return t;
-}
-
-// One packed word (8 codes, element 2i in the low nibble of byte i) -> 8 bf16
-// in the order 0 2 | 4 6 | 1 3 | 5 7 (pairs per dword, low half first).
-__device__ __forceinline__ u32x4 decode8_perm(uint32_t d, const PermTable& t) {
-  const uint32_t n8 = d & 0x88888888u;                   // bit 3 of every code
-  const uint32_t x = d ^ (n8 - (n8 >> 3));               // c XOR 7b per nibble
-  const uint32_t se = x & 0x07070707u;                   // magnitude index, even elements
-  const uint32_t so = (x >> 4) & 0x07070707u;            // odd elements
-  const uint32_t nd = ~d;                                // bit 3 clear <=> negative level
-  const uint32_t loE = perm(t.lo1, t.lo0, se);
-  const uint32_t hiE = perm(t.hi1, t.hi0, se) | ((nd << 4) & 0x80808080u);
-  const uint32_t loO = perm(t.lo1, t.lo0, so);
-  const uint32_t hiO = perm(t.hi1, t.hi0, so) | (nd & 0x80808080u);
-  u32x4 r;
-  r.x = perm(hiE, loE, 0x05010400u);
-  r.y = perm(hiE, loE, 0x07030602u);
-  r.z = perm(hiO, loO, 0x05010400u);
-  r.w = perm(hiO, loO, 0x07030602u);
-  return r;
-}
 
 // 8 consecutive bf16 (4 dwords, low half first) -> the order 0 2 | 4 6 | 1 3 | 5 7
 __device__ __forceinline__ u32x4 perm8(const u32x4& v) {
@@ -330,7 +291,7 @@ __global__ __launch_bounds__(256, 2) void k_dec_fwd(DecFwdBatch bt, Codebook cb)
       } else {
         sc = kvalid ? block_scale(static_cast<int8_t>(cur.q[nt]), cur.d[nt]) : 0.0f;
       }
-      const PermTable tb = make_ptable(cb, sc);
+      const MagTable tb = make_table(cb, sc);
       const uint32_t pw[8] = {cur.cw[nt][0].x, cur.cw[nt][0].y, cur.cw[nt][0].z, cur.cw[nt][0].w,
                               cur.cw[nt][1].x, cur.cw[nt][1].y, cur.cw[nt][1].z, cur.cw[nt][1].w};
 #pragma unroll

@@ -42,16 +42,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float bf16_lo(uint32_t p) { return __builtin_bit_cast(float, p << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t p) { return __builtin_bit_cast(float, p & 0xFFFF0000u); }
 
-// Per-block magnitude table in byte planes: entry i = bf16(L[8+i] * s).
+// Per-block magnitude table in byte planes: entry j (0..7) = bf16(L[15-j] * s),
+// the magnitudes largest first; low and high bytes in two dwords each.
 struct MagTable {
   uint32_t lo0, lo1, hi0, hi1;
 };
 
 __device__ __forceinline__ MagTable make_table(const Codebook& cb, float s) {
-  const uint32_t p0 = pack_bf16x2(cb.L[8] * s, cb.L[9] * s);
-  const uint32_t p1 = pack_bf16x2(cb.L[10] * s, cb.L[11] * s);
-  const uint32_t p2 = pack_bf16x2(cb.L[12] * s, cb.L[13] * s);
-  const uint32_t p3 = pack_bf16x2(cb.L[14] * s, cb.L[15] * s);
+  const uint32_t p0 = pack_bf16x2(cb.L[15] * s, cb.L[14] * s);
+  const uint32_t p1 = pack_bf16x2(cb.L[13] * s, cb.L[12] * s);
+  const uint32_t p2 = pack_bf16x2(cb.L[11] * s, cb.L[10] * s);
+  const uint32_t p3 = pack_bf16x2(cb.L[9] * s, cb.L[8] * s);
   MagTable t;
   t.lo0 = perm(p1, p0, 0x06040200u);
   t.hi0 = perm(p1, p0, 0x07050301u);
@@ -60,33 +61,63 @@ __device__ __forceinline__ MagTable make_table(const Codebook& cb, float s) {
   return t;
 }
 
-// Four codes, one per byte (values 0..15 in bits 0-3; bit 3 also given by
-// `pos` = 1 per byte when the code is >= 8): low and high bf16 byte planes.
-//   code >= 8: magnitude index code-8 = code ^ 8, positive
-//   code <  8: magnitude index 7-code = code ^ 7, negative
-__device__ __forceinline__ void lookup4(uint32_t codes, uint32_t pos, const MagTable& t,
-                                        uint32_t& lo, uint32_t& hi) {
-  const uint32_t mi = (codes ^ (pos + 0x07070707u)) & 0x07070707u;
-  lo = perm(t.lo1, t.lo0, mi);
-  hi = perm(t.hi1, t.hi0, mi) ^ ((pos ^ 0x01010101u) << 7);
+// v_bitop3_b32 with truth table kTT (bit 4a + 2b + c of kTT is the result for
+// input bits a, b, c). Called by name because the compiler rewrites the masked
+// forms below into sequences one or two operations longer.
+template <int kTT>
+__device__ __forceinline__ uint32_t bitop3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, kTT);
+}
+constexpr int kTTXorAnd = 0x28;      // (a ^ b) & c
+constexpr int kTTOrAndNot = 0xF2;    // a | (~b & c)
+
+// The byte planes of the 8 codes of one packed dword (element 2i in the low
+// nibble of byte i): even elements (0 2 4 6) in loE/hiE, odd ones in loO/hiO.
+// Code c maps to magnitude index c (c < 8) or 15 - c (c >= 8), i.e. c XOR 7b
+// with b = bit 3 of c, masked to 3 bits, for all eight nibbles at once; the
+// sign bit of the high byte is set where bit 3 of the code is clear.
+struct Planes {
+  uint32_t loE, hiE, loO, hiO;
+};
+__device__ __forceinline__ Planes lookup8(uint32_t d, const MagTable& t) {
+  const uint32_t n8 = d & 0x88888888u;                   // bit 3 of every code
+  const uint32_t f = n8 - (n8 >> 3);                     // 7 in every nibble with bit 3 set
+  const uint32_t se = bitop3<kTTXorAnd>(d, f, 0x07070707u);
+  const uint32_t so = bitop3<kTTXorAnd>(d, f, 0x70707070u) >> 4;
+  Planes p;
+  p.loE = perm(t.lo1, t.lo0, se);
+  p.hiE = bitop3<kTTOrAndNot>(perm(t.hi1, t.hi0, se), d << 4, 0x80808080u);
+  p.loO = perm(t.lo1, t.lo0, so);
+  p.hiO = bitop3<kTTOrAndNot>(perm(t.hi1, t.hi0, so), d, 0x80808080u);
+  return p;
 }
 
-// One packed dword (8 codes, element 2i in the low nibble of byte i) ->
-// 8 bf16 in natural order, as 4 dwords of bf16 pairs.
+// One packed dword -> 8 bf16 in natural order, as 4 dwords of bf16 pairs
+// (21 VALU operations).
 __device__ __forceinline__ u32x4 decode8(uint32_t d, const MagTable& t) {
-  uint32_t loE, hiE, loO, hiO;
-  lookup4(d, (d >> 3) & 0x01010101u, t, loE, hiE);          // even elements
-  lookup4(d >> 4, (d >> 7) & 0x01010101u, t, loO, hiO);     // odd elements
-  // interleave: [lo e0, lo e1, lo e2, lo e3] etc., then lo/hi into pairs
-  const uint32_t l03 = perm(loO, loE, 0x05010400u);
-  const uint32_t l47 = perm(loO, loE, 0x07030602u);
-  const uint32_t h03 = perm(hiO, hiE, 0x05010400u);
-  const uint32_t h47 = perm(hiO, hiE, 0x07030602u);
+  const Planes p = lookup8(d, t);
+  // interleave even and odd elements per plane, then pair low and high bytes
+  const uint32_t l03 = perm(p.loO, p.loE, 0x05010400u);
+  const uint32_t l47 = perm(p.loO, p.loE, 0x07030602u);
+  const uint32_t h03 = perm(p.hiO, p.hiE, 0x05010400u);
+  const uint32_t h47 = perm(p.hiO, p.hiE, 0x07030602u);
   u32x4 r;
   r.x = perm(h03, l03, 0x05010400u);
   r.y = perm(h03, l03, 0x07030602u);
   r.z = perm(h47, l47, 0x05010400u);
   r.w = perm(h47, l47, 0x07030602u);
+  return r;
+}
+
+// The same 8 bf16 in the order 0 2 | 4 6 | 1 3 | 5 7 (17 VALU operations):
+// for contractions whose other operand is permuted the same way.
+__device__ __forceinline__ u32x4 decode8_perm(uint32_t d, const MagTable& t) {
+  const Planes p = lookup8(d, t);
+  u32x4 r;
+  r.x = perm(p.hiE, p.loE, 0x05010400u);
+  r.y = perm(p.hiE, p.loE, 0x07030602u);
+  r.z = perm(p.hiO, p.loO, 0x05010400u);
+  r.w = perm(p.hiO, p.loO, 0x07030602u);
   return r;
 }
 

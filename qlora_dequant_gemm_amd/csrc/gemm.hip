@@ -565,6 +565,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd(const uint16_t* __restrict_
     bf16x8 af[2][4], bf[2][4];
     read_a(Ab, 0, af[0]);
     read_b(Wb, 0, bf[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    // Each sub-step is its own scheduling region, issued in this order: its
+    // first MFMA (operands read during the previous sub-step), then per MFMA
+    // one fragment read of the next sub-step and three VALU ops of the
+    // decode, then its W' writes (and in the last one the dY writes). Left
+    // free, the scheduler pulls MFMAs of later sub-steps forward, and those
+    // then wait for reads issued only just before.
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (s < 3) {
@@ -578,31 +585,18 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd(const uint16_t* __restrict_
 #pragma unroll
       for (int c = 0; c < 2; ++c) Wn[w_slot(brow, 8 * bkb + 2 * s + c)] = decode8(pw[2 * s + c], tb);
       if (s == 3) store_a(An);
-    }
-    // issue order: all fragment reads of a sub-step at the start of the one
-    // before it (the compiler waits for ds_read_b64_tr_b16 with lgkmcnt(0) at
-    // the first use, so they must be long in flight by then), then per MFMA
-    // about four VALU ops of the decode; each sub-step's two W' writes at its
-    // end and the eight dY writes in the last sub-step. (Mask 0x080, all LDS
-    // ops: the transposed reads do not count as plain LDS reads.)
-    auto sub_mfmas = [] {
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        if (s < 3 && m < 12) __builtin_amdgcn_sched_group_barrier(0x080, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
       }
-    };
-    __builtin_amdgcn_sched_group_barrier(0x080, 24, 0);
-    sub_mfmas();
-    __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x080, 12, 0);
-    sub_mfmas();
-    __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x080, 12, 0);
-    sub_mfmas();
-    __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
-    sub_mfmas();
-    __builtin_amdgcn_sched_group_barrier(0x200, 10, 0);
+      if (s == 3)
+        __builtin_amdgcn_sched_group_barrier(0x200, 10, 0);
+      else
+        __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   // prologue: dY tile 0, codes of steps 0 and 1; decode step 0
