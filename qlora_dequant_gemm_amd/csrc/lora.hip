@@ -98,6 +98,90 @@ __global__ __launch_bounds__(256) void k_down(const uint16_t* in, int64_t M, int
   }
 }
 
+// ---------------------------------------------------------------------------
+// Row-streaming form for the matmul paths (M > 16, output [M][rp]): one
+// workgroup per 16 rows of `in`, its eight waves taking interleaved 64-deep
+// chunks of the contraction (wave w: chunks w, w + 8, ...), so the workgroup
+// streams its rows front to back with 8 GS chunks of each row in flight and
+// no split partials leave the chip; the eight waves' 16 x 16 RT accumulators
+// are summed through LDS in wave order.
+// 16x16x32 bf16 MFMA: in a 64-deep chunk, lane (g, c) supplies row c's
+// elements [16 g, 16 g + 16) as the k-slots of two MFMAs, and the adapter
+// row 16 jt + c the same elements (a contraction is order-free). Kc % 8 == 0:
+// 8-element pieces past Kc are zeroed; rows past M and adapter rows past r
+// read as zero through the descriptors.
+// ---------------------------------------------------------------------------
+constexpr int kDownWaves = 8;
+
+template <int RT, int GS>
+__global__ __launch_bounds__(64 * kDownWaves) void k_down_rows(const uint16_t* in, int M, int Kc, const uint16_t* W, int r,
+                                                   int rp, uint16_t* __restrict__ out) {
+  __shared__ f32x4 red[kDownWaves][RT][64];
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int m0 = blockIdx.x * 16;
+  const int rows_valid = M - m0 < 16 ? M - m0 : 16;
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(in + static_cast<int64_t>(m0) * Kc), 0, rows_valid * Kc * 2, kBufWord3);
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(W), 0, r * Kc * 2,
+                                                                      kBufWord3);
+  const int nchunk = (Kc + 63) / 64;
+  const uint32_t xo = static_cast<uint32_t>((c * Kc + 16 * g) * 2);
+  uint32_t wo[RT];
+#pragma unroll
+  for (int jt = 0; jt < RT; ++jt) wo[jt] = static_cast<uint32_t>(((16 * jt + c) * Kc + 16 * g) * 2);
+  f32x4 acc[RT];
+#pragma unroll
+  for (int jt = 0; jt < RT; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  // GS chunks per round, all their loads issued before their MFMAs
+  for (int q0 = w; q0 < nchunk; q0 += kDownWaves * GS) {
+    u32x4 xa[GS][2], wa[GS][RT][2];
+#pragma unroll
+    for (int u = 0; u < GS; ++u) {
+      const int q = q0 + kDownWaves * u < nchunk ? q0 + kDownWaves * u : nchunk - 1;
+      const uint32_t so = static_cast<uint32_t>(q * 128);
+      xa[u][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xo, so, 0));
+      xa[u][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xo + 16, so, 0));
+#pragma unroll
+      for (int jt = 0; jt < RT; ++jt) {
+        wa[u][jt][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, wo[jt], so, 0));
+        wa[u][jt][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, wo[jt] + 16, so, 0));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < GS; ++u) {
+      const int q = q0 + kDownWaves * u;
+      const int k = q * 64 + 16 * g;
+      // a repeated last chunk, or pieces past Kc, contribute nothing
+      const bool live0 = q < nchunk && k < Kc, live1 = q < nchunk && k + 8 < Kc;
+      const u32x4 x0 = live0 ? xa[u][0] : zero, x1 = live1 ? xa[u][1] : zero;
+#pragma unroll
+      for (int jt = 0; jt < RT; ++jt) {
+        acc[jt] = mfma16(as_bf16x8(x0), as_bf16x8(live0 ? wa[u][jt][0] : zero), acc[jt]);
+        acc[jt] = mfma16(as_bf16x8(x1), as_bf16x8(live1 ? wa[u][jt][1] : zero), acc[jt]);
+      }
+    }
+  }
+#pragma unroll
+  for (int jt = 0; jt < RT; ++jt) red[w][jt][lane] = acc[jt];
+  __syncthreads();
+  // lane (g, c) of a fragment holds rows 4 g + v, rank 16 jt + c
+  for (int e = t; e < 16 * rp; e += 64 * kDownWaves) {
+    const int row = e / rp, j = e - (e / rp) * rp;
+    if (row >= rows_valid) continue;
+    float sum = 0.f;
+    if (j < 16 * RT) {
+      const int jt = j >> 4, l = ((row >> 2) << 4) | (j & 15);
+      const int v = row & 3;
+#pragma unroll
+      for (int ww = 0; ww < kDownWaves; ++ww) sum += red[ww][jt][l][v];
+    }
+    out[static_cast<int64_t>(m0 + row) * rp + j] = bf16_bits(sum);
+  }
+}
+
 // Sum of the KS split partials in order, rounded to bf16, written [M][rp] or
 // transposed [rp][ldt] (rows past M and ranks past 16 nt zero).
 __global__ __launch_bounds__(256) void k_down_finish(const float* __restrict__ part, int KS, int64_t M,
@@ -140,6 +224,26 @@ hipError_t launch_lora_down(bool wrow, const uint16_t* in, int64_t M, int64_t Kc
   if (!wrow) {
     hipLaunchKernelGGL(k_adapter_t, dim3(static_cast<unsigned>(cdiv(Kc, 64))), dim3(256), 0, stream, W, Kc, r, wt);
     Wr = wt;
+  }
+  if (!ldt && M > 16) {
+    // the matmul paths: row-streaming form, no split partials
+    const unsigned grid16 = static_cast<unsigned>(cdiv(M, 16));
+    const int mi = static_cast<int>(M), kci = static_cast<int>(Kc);
+    uint16_t* o16 = static_cast<uint16_t*>(out);
+    const int nt = down_nt(r);
+    if (nt == 1)
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(k_down_rows<1, 4>), dim3(grid16), dim3(64 * kDownWaves), 0, stream, in, mi, kci, Wr, r,
+                         rp, o16);
+    else if (nt == 2)
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(k_down_rows<2, 4>), dim3(grid16), dim3(64 * kDownWaves), 0, stream, in, mi, kci, Wr, r,
+                         rp, o16);
+    else if (nt == 4)
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(k_down_rows<4, 2>), dim3(grid16), dim3(64 * kDownWaves), 0, stream, in, mi, kci, Wr, r,
+                         rp, o16);
+    else
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(k_down_rows<8, 1>), dim3(grid16), dim3(64 * kDownWaves), 0, stream, in, mi, kci, Wr, r,
+                         rp, o16);
+    return hipGetLastError();
   }
   const DownPlan p = down_plan(M, Kc, r);
   const unsigned grid = static_cast<unsigned>(cdiv(M, 64) * p.KS);
