@@ -100,7 +100,8 @@ struct BScale4 {   // the same for the four steps of a super-step
 // super-step are one aligned 4-byte word of qscale and share one second-level
 // step (a 256-block group never splits 4-aligned blocks); scales are then
 // loaded once per super-step. Otherwise they are loaded per step.
-template <bool kQuad>
+// RSN: rank_pad(r) / 16 (chunks of 16 ranks in the LoRA epilogue), 0 for none.
+template <bool kQuad, int RSN>
 __global__ __launch_bounds__(256, 1) void k_gemm_fwd(const uint16_t* __restrict__ x, int64_t M, int64_t N,
                                                      int64_t K, const uint8_t* __restrict__ packed,
                                                      const int8_t* __restrict__ qscale,
@@ -375,27 +376,46 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd(const uint16_t* __restrict_
   }
   wait_vm<0>();
 
-  // epilogue: LoRA up-projection as a rank-r MFMA, then bf16 stores
-  if (r > 0) {
+  // epilogue: LoRA up-projection as a rank-r MFMA (RSN chunks of 16 ranks),
+  // then bf16 stores
+  if constexpr (RSN > 0) {
     const bool vec_ok = (r & 7) == 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t mrow = imin(m0 + 32 * i + l32, M - 1);
+    // All fragment loads of a group of row blocks go out before its MFMAs,
+    // so their latency is paid once, not once per MFMA.
+    auto lora = [&](auto rsn_c) {
+      constexpr int RS = decltype(rsn_c)::value;
+      constexpr int IG = RS <= 2 ? 8 : RS <= 4 ? 4 : 2;   // row blocks per group (registers)
+      u32x4 bfr[2][RS];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int64_t nrow = imin(n0 + 64 * w + 32 * j + l32, N - 1);
-        f32x16 tmp;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) tmp[v] = 0.f;
-        for (int rs = 0; rs < rp / 16; ++rs) {
-          const bf16x8 a = as_bf16x8(ld16(tl + mrow * rp + 16 * rs + 8 * h));
-          const bf16x8 b = as_bf16x8(load_row8(Bl + nrow * r, 16 * rs + 8 * h, r, vec_ok));
-          tmp = mfma32(a, b, tmp);
+        for (int rs = 0; rs < RS; ++rs) bfr[j][rs] = load_row8(Bl + nrow * r, 16 * rs + 8 * h, r, vec_ok);
+      }
+#pragma unroll
+      for (int i0 = 0; i0 < 8; i0 += IG) {
+        u32x4 tf[IG][RS];
+#pragma unroll
+        for (int ii = 0; ii < IG; ++ii) {
+          const int64_t mrow = imin(m0 + 32 * (i0 + ii) + l32, M - 1);
+#pragma unroll
+          for (int rs = 0; rs < RS; ++rs) tf[ii][rs] = ld16(tl + mrow * rp + 16 * rs + 8 * h);
         }
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] += scale * tmp[v];
+        for (int ii = 0; ii < IG; ++ii)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            f32x16 tmp;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) tmp[v] = 0.f;
+#pragma unroll
+            for (int rs = 0; rs < RS; ++rs) tmp = mfma32(as_bf16x8(tf[ii][rs]), as_bf16x8(bfr[j][rs]), tmp);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i0 + ii][j][v] += scale * tmp[v];
+          }
       }
-    }
+    };
+    lora(std::integral_constant<int, RSN>{});
   }
   // bf16 stores: for fixed (i, j, v) the 32 lanes of a half-wave write 64
   // contiguous bytes of one row; interior tiles skip the bounds checks
@@ -451,6 +471,7 @@ struct BCodes {
   float live;      // 1 for a real weight row, 0 past N
 };
 
+template <int RSN>
 __global__ __launch_bounds__(256, 1) void k_gemm_bwd(const uint16_t* __restrict__ dy, int64_t M, int64_t N,
                                                      int64_t K, const uint8_t* __restrict__ packed,
                                                      const int8_t* __restrict__ qscale,
@@ -629,31 +650,71 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd(const uint16_t* __restrict_
   }
   wait_vm<0>();
 
-  if (r > 0) {
+  if constexpr (RSN > 0) {
+    // The up-projection needs A transposed (ranks along the contraction): the
+    // r x 256 block of A under this tile goes through the LDS, free after the
+    // main loop, as At[col][rank] with rows of rp + 8 elements (16-byte
+    // aligned; the pad spreads a read phase over more banks). Ranks past r
+    // and columns past K are zero.
+    __syncthreads();
+    uint16_t* At = reinterpret_cast<uint16_t*>(As0);
+    const int atw = rp + 8;
+    {
+      // 16 RSN rows x 32 chunks of 8 columns: every load issued before any
+      // LDS write (K % 64 == 0, so a chunk is wholly inside or past K)
+      constexpr int kPer = 16 * RSN * 32 / 256;
+      u32x4 av[kPer];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t mrow = imin(m0 + 128 * wm + 32 * i + l32, M - 1);
+      for (int u = 0; u < kPer; ++u) {
+        const int e = t + 256 * u, j = e >> 5, c8 = (e & 31) * 8;
+        const int64_t kc = k0 + c8;
+        av[u] = (j < r && kc < K) ? ld16(Al + static_cast<int64_t>(j) * K + kc) : u32x4{0u, 0u, 0u, 0u};
+      }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t kcol = imin(k0 + 128 * wn + 32 * j + l32, K - 1);
-        f32x16 tmp;
+      for (int u = 0; u < kPer; ++u) {
+        const int e = t + 256 * u, j = e >> 5, c8 = (e & 31) * 8;
+        const uint32_t wv[4] = {av[u].x, av[u].y, av[u].z, av[u].w};
 #pragma unroll
-        for (int v = 0; v < 16; ++v) tmp[v] = 0.f;
-        for (int rs = 0; rs < rp / 16; ++rs) {
-          const bf16x8 a = as_bf16x8(ld16(ul + mrow * rp + 16 * rs + 8 * h));
-          uint32_t bv[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int jj = 16 * rs + 8 * h + e;
-            const uint32_t val = jj < r ? static_cast<uint32_t>(Al[static_cast<int64_t>(jj) * K + kcol]) : 0u;
-            bv[e >> 1] |= val << (16 * (e & 1));
-          }
-          tmp = mfma32(a, as_bf16x8(u32x4{bv[0], bv[1], bv[2], bv[3]}), tmp);
-        }
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] += scale * tmp[v];
+        for (int q = 0; q < 8; ++q)
+          At[(c8 + q) * atw + j] = static_cast<uint16_t>(wv[q >> 1] >> (16 * (q & 1)));
       }
     }
+    __syncthreads();
+    auto lora = [&](auto rsn_c) {
+      constexpr int RS = decltype(rsn_c)::value;
+      constexpr int JG = RS <= 2 ? 4 : 2;             // column blocks per group (registers)
+      u32x4 uf[4][RS];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t mrow = imin(m0 + 128 * wm + 32 * i + l32, M - 1);
+#pragma unroll
+        for (int rs = 0; rs < RS; ++rs) uf[i][rs] = ld16(ul + mrow * rp + 16 * rs + 8 * h);
+      }
+#pragma unroll
+      for (int j0 = 0; j0 < 4; j0 += JG) {
+        u32x4 af[JG][RS];
+#pragma unroll
+        for (int jj = 0; jj < JG; ++jj) {
+          const int col = 128 * wn + 32 * (j0 + jj) + l32;
+#pragma unroll
+          for (int rs = 0; rs < RS; ++rs)
+            af[jj][rs] = *reinterpret_cast<const u32x4*>(At + col * atw + 16 * rs + 8 * h);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int jj = 0; jj < JG; ++jj) {
+            f32x16 tmp;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) tmp[v] = 0.f;
+#pragma unroll
+            for (int rs = 0; rs < RS; ++rs) tmp = mfma32(as_bf16x8(uf[i][rs]), as_bf16x8(af[jj][rs]), tmp);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j0 + jj][v] += scale * tmp[v];
+          }
+      }
+    };
+    lora(std::integral_constant<int, RSN>{});
   }
   if (m0 + kTile <= M && k0 + kTile <= K) {
     uint16_t* dt = dx + (m0 + 128 * wm + 4 * h) * K + k0 + 128 * wn + l32;
@@ -699,12 +760,26 @@ hipError_t launch_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K, c
     if (e != hipSuccess) return e;
   }
   const int64_t tiles = cdiv(M, kTile) * cdiv(N, kTile);
-  if (K % 256 == 0)
-    hipLaunchKernelGGL(k_gemm_fwd<true>, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, x, M, N, K,
-                       packed, qscale, step, static_cast<const uint16_t*>(lora), rp, B, r, scale, y, cb);
-  else
-    hipLaunchKernelGGL(k_gemm_fwd<false>, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, x, M, N, K,
-                       packed, qscale, step, static_cast<const uint16_t*>(lora), rp, B, r, scale, y, cb);
+  const bool quad = K % 256 == 0;
+#define QNF4_FWD(RSNV)                                                                                          \
+  do {                                                                                                         \
+    if (quad)                                                                                                  \
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_fwd<true, RSNV>), dim3(static_cast<unsigned>(tiles)), dim3(256), \
+                         0, stream, x, M, N, K, packed, qscale, step, static_cast<const uint16_t*>(lora), rp, B, \
+                         r, scale, y, cb);                                                                     \
+    else                                                                                                       \
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_fwd<false, RSNV>), dim3(static_cast<unsigned>(tiles)),          \
+                         dim3(256), 0, stream, x, M, N, K, packed, qscale, step,                               \
+                         static_cast<const uint16_t*>(lora), rp, B, r, scale, y, cb);                          \
+  } while (0)
+  switch (rp / 16) {
+    case 0: QNF4_FWD(0); break;
+    case 2: QNF4_FWD(2); break;
+    case 4: QNF4_FWD(4); break;
+    case 6: QNF4_FWD(6); break;
+    default: QNF4_FWD(8); break;
+  }
+#undef QNF4_FWD
   return hipGetLastError();
 }
 
@@ -752,8 +827,17 @@ hipError_t launch_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K, co
     if (e != hipSuccess) return e;
   }
   const int64_t tiles = cdiv(M, kTile) * cdiv(K, kTile);
-  hipLaunchKernelGGL(k_gemm_bwd, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, dy, M, N, K, packed,
-                     qscale, step, static_cast<const uint16_t*>(lora), rp, A, r, scale, dx, cb);
+#define QNF4_BWD(RSNV)                                                                                         \
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_bwd<RSNV>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, \
+                     dy, M, N, K, packed, qscale, step, static_cast<const uint16_t*>(lora), rp, A, r, scale, dx, cb)
+  switch (rp / 16) {
+    case 0: QNF4_BWD(0); break;
+    case 2: QNF4_BWD(2); break;
+    case 4: QNF4_BWD(4); break;
+    case 6: QNF4_BWD(6); break;
+    default: QNF4_BWD(8); break;
+  }
+#undef QNF4_BWD
   return hipGetLastError();
 }
 
