@@ -489,6 +489,7 @@ def run_gpu(args):
                           "hbm_frac": round(work[0] / ms / 1e6 / HBM_PEAK_GBS, 4),
                           "TFLOP/s": round(work[1] / ms / 1e9, 2)}
     wl.extra = extra
+    wl.kernel_ms = kernel_times(wl, stream, max(wl.Ms))
     wl.decode_result = decode_walks(wl, stream) if isinstance(wl, StackWorkload) else None
     return wl, ms_step, per_call, wall
 
@@ -701,6 +702,52 @@ CALL_KERNEL = {"quantize_dq": ("k_quantize", "quant.hip"), "fwd": ("k_dec_fwd", 
                "bwd_big": ("k_gemm_bwd", "gemm.hip")}
 
 
+def kernel_times(wl, stream, M, reps_max=32):
+    """Per call label whose main kernel is a matmul: ms of that kernel alone,
+    from two HIP events the library records on the launch stream right
+    before and after it (qlora_set_kernel_events), averaged over the label's
+    calls issued one at a time."""
+    import ctypes
+    import torch
+    from qlora_dequant_gemm_amd import _lib
+    hip = ctypes.CDLL("libamdhip64.so")
+    for fn in ("hipEventCreate", "hipEventSynchronize", "hipEventElapsedTime", "hipEventDestroy"):
+        getattr(hip, fn).restype = ctypes.c_int
+    hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    e0, e1 = ctypes.c_void_p(), ctypes.c_void_p()
+    if hip.hipEventCreate(ctypes.byref(e0)) or hip.hipEventCreate(ctypes.byref(e1)):
+        raise RuntimeError("hipEventCreate failed")
+    L = _lib.lib()
+    out = {}
+    try:
+        for lab, fns in wl.timing_groups():
+            if kernel_of(lab, M)[0] == "k_quantize":
+                continue
+            with torch.cuda.stream(stream):
+                fns[0]()
+            torch.cuda.synchronize()
+            L.qlora_set_kernel_events(e0, e1)
+            tot, n = 0.0, 0
+            for fn in fns[:reps_max]:
+                with torch.cuda.stream(stream):
+                    fn()
+                ms = ctypes.c_float()
+                if hip.hipEventSynchronize(e1) or hip.hipEventElapsedTime(ctypes.byref(ms), e0, e1):
+                    raise RuntimeError(f"kernel events of {lab} not recorded")
+                tot += ms.value
+                n += 1
+            L.qlora_set_kernel_events(None, None)
+            out[lab] = tot / n
+    finally:
+        L.qlora_set_kernel_events(None, None)
+        torch.cuda.synchronize()
+        hip.hipEventDestroy(e0)
+        hip.hipEventDestroy(e1)
+    return out
+
+
 def kernel_of(label, M):
     """(kernel, source) that does the arithmetic of a call label."""
     key = label if label == "quantize_dq" else label.split("_")[0]
@@ -776,12 +823,16 @@ def main():
         b, f = wk[lab]
         kernels[lab] = {"ms": round(ms, 5), "GB/s": round(b / ms / 1e6, 1),
                         "hbm_frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4)}
+        if lab in wl.kernel_ms:
+            kernels[lab]["kernel_ms"] = round(wl.kernel_ms[lab], 5)
         if f:
             kernels[lab]["TFLOP/s"] = round(f / ms / 1e9, 2)
     # the roofline kernel: the one with the largest share of the step's time
-    # (per-call time x calls per step, summed over the calls that run it)
+    # (its own launch time x calls per step, summed over the calls that run
+    # it; per-call time where a call has no marked kernel)
     share = {}
-    for lab, ms in per_call.items():
+    for lab, call_ms in per_call.items():
+        ms = wl.kernel_ms.get(lab, call_ms)
         kn = kernel_of(lab, max(wl.Ms))
         n = wl.calls_per_step(lab) if hasattr(wl, "calls_per_step") else 1
         t, b_, f_, labs = share.get(kn, (0.0, 0.0, 0.0, []))
@@ -789,8 +840,12 @@ def main():
     (kname, unit_src), (t_k, b_k, f_k, labs_k) = max(share.items(), key=lambda kv: kv[1][0])
     traffic = read_traffic(kname, unit_src, wl.name)
     n_launch = sum(wl.calls_per_step(l) if hasattr(wl, "calls_per_step") else 1 for l in labs_k)
+    call_ms = sum((wl.calls_per_step(l) if hasattr(wl, "calls_per_step") else 1) * per_call[l] for l in labs_k)
     common = {"traffic": traffic, "kernel": kname, "calls": labs_k, "launches_per_step": n_launch,
-              "ms_per_launch": round(t_k / n_launch, 5), "step_time_share": round(t_k / ms_step, 4)}
+              "ms_per_launch": round(t_k / n_launch, 5), "step_time_share": round(t_k / ms_step, 4),
+              "timing": "kernel alone, between HIP events the library records around its launch on the call's "
+                        "stream (qlora_set_kernel_events), averaged over the calls",
+              "call_ms_per_launch": round(call_ms / n_launch, 5)}
     if wl.decode or kname == "k_quantize":
         ach = b_k / t_k / 1e6
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -365,6 +365,20 @@ int qlora_nf4_codebook(float levels[16], float thresholds[15]);
 /* Human-readable name of a qlora_status value (static storage). */
 const char* qlora_status_string(int status);
 
+/*
+ * Measurement aid for profilers and benchmarks (not needed for computing):
+ * while set, every matmul call records `start` (a hipEvent_t created by the
+ * caller) on its stream right before launching its main kernel -- the tiled
+ * GEMM, the decode-shaped kernel (the batched forward: before its first
+ * launch), or the small-M backward kernel -- and `stop` right after it (after
+ * the last launch), so that hipEventElapsedTime(start, stop) is that kernel's
+ * duration without the LoRA down-projection or finishing launches of the same
+ * call. Both NULL stops it; exactly one NULL returns QLORA_ERR_NULL. The
+ * setting is process-wide: calls on other threads or streams record the same
+ * events while it is set.
+ */
+int qlora_set_kernel_events(void* start, void* stop);
+
 /* hipError_t of the most recent QLORA_ERR_HIP on the calling thread. */
 int qlora_last_hip_error(void);
 

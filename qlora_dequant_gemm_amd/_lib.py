@@ -26,6 +26,7 @@ SIGNATURES = [
     ("qlora_workspace_bytes", _sz, [_i32, _i64, _i64, _i64, _i32]),
     ("qlora_nf4_lora_fwd", _i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _f32,
                                   _vp, _vp, _sz, _vp]),
+    ("qlora_set_kernel_events", _i32, [_vp, _vp]),
     ("qlora_nf4_lora_fwd_noalloc", _i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _f32,
                                           _vp, _vp]),
     ("qlora_nf4_lora_fwd_grouped", _i32, [_vp, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32,

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/qlora_nf4.h"
 #include "codebook.hpp"
 #include "kernels.hpp"
@@ -60,7 +62,16 @@ int check_ws(void* ws, size_t ws_bytes, size_t need) {
   return QLORA_OK;
 }
 
+std::atomic<void*> g_kev_start{nullptr}, g_kev_stop{nullptr};
+
 }  // namespace
+
+namespace qnf4 {
+void mark_kernel(int which, hipStream_t stream) {
+  void* e = (which == 0 ? g_kev_start : g_kev_stop).load(std::memory_order_relaxed);
+  if (e) (void)hipEventRecord(static_cast<hipEvent_t>(e), stream);
+}
+}  // namespace qnf4
 
 extern "C" {
 
@@ -83,6 +94,13 @@ const char* qlora_status_string(int status) {
 }
 
 int qlora_last_hip_error(void) { return g_last_hip_error; }
+
+int qlora_set_kernel_events(void* start, void* stop) {
+  if ((start == nullptr) != (stop == nullptr)) return QLORA_ERR_NULL;
+  g_kev_start.store(start, std::memory_order_relaxed);
+  g_kev_stop.store(stop, std::memory_order_relaxed);
+  return QLORA_OK;
+}
 
 int qlora_nf4_codebook(float levels[16], float thresholds[15]) {
   if (!levels || !thresholds) return QLORA_ERR_NULL;

@@ -502,6 +502,7 @@ hipError_t launch_dec_fwd(int64_t M, int G, const uint16_t* const* x, const int6
                           uint16_t* const* y, void* ws, const Codebook& cb, hipStream_t stream) {
   char* wsb = static_cast<char*>(ws);
   const int RT = r <= 0 ? 0 : r <= 16 ? 1 : r <= 32 ? 2 : r <= 64 ? 4 : 8;
+  mark_kernel(0, stream);
   for (int c0 = 0; c0 < G; c0 += kDecMaxProblems) {
     const int cn = G - c0 < kDecMaxProblems ? G - c0 : kDecMaxProblems;
     const DecChunkPlan pl = dec_plan_chunk(M, cn, N + c0, K + c0);
@@ -557,6 +558,7 @@ hipError_t launch_dec_fwd(int64_t M, int G, const uint16_t* const* x, const int6
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  mark_kernel(1, stream);
   return hipSuccess;
 }
 

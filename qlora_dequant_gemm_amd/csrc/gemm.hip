@@ -772,6 +772,7 @@ hipError_t launch_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K, c
                          dim3(256), 0, stream, x, M, N, K, packed, qscale, step,                               \
                          static_cast<const uint16_t*>(lora), rp, B, r, scale, y, cb);                          \
   } while (0)
+  mark_kernel(0, stream);
   switch (rp / 16) {
     case 0: QNF4_FWD(0); break;
     case 2: QNF4_FWD(2); break;
@@ -780,6 +781,7 @@ hipError_t launch_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K, c
     default: QNF4_FWD(8); break;
   }
 #undef QNF4_FWD
+  mark_kernel(1, stream);
   return hipGetLastError();
 }
 
@@ -830,6 +832,7 @@ hipError_t launch_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K, co
 #define QNF4_BWD(RSNV)                                                                                         \
   hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_bwd<RSNV>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, \
                      dy, M, N, K, packed, qscale, step, static_cast<const uint16_t*>(lora), rp, A, r, scale, dx, cb)
+  mark_kernel(0, stream);
   switch (rp / 16) {
     case 0: QNF4_BWD(0); break;
     case 2: QNF4_BWD(2); break;
@@ -838,6 +841,7 @@ hipError_t launch_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K, co
     default: QNF4_BWD(8); break;
   }
 #undef QNF4_BWD
+  mark_kernel(1, stream);
   return hipGetLastError();
 }
 

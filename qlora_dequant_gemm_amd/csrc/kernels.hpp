@@ -200,6 +200,11 @@ hipError_t launch_lora_grad(const uint16_t* x, const uint16_t* dy, int64_t M, in
                             const uint16_t* A, const uint16_t* B, int r, float alpha, float* dA, float* dB,
                             int accumulate, void* ws, hipStream_t stream);
 
+// Measurement events (set through the C ABI): when set, mark_kernel(0, s)
+// records the start event and mark_kernel(1, s) the stop event on stream s,
+// right around the main kernel of a matmul call.
+void mark_kernel(int which, hipStream_t stream);
+
 // Built-in scratch of the allocation-free forward: a file-scope device array
 // of kNoAllocScratchBytes per GPU. noalloc_scratch gives this device's address
 // of it (looked up once per device, on the first call with that device

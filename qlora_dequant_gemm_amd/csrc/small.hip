@@ -229,6 +229,7 @@ hipError_t launch_bwd_small(const uint16_t* dy, int64_t M, int64_t N, int64_t K,
 #define QNF4_BWDS(NTV)                                                                                        \
   hipLaunchKernelGGL(k_bwd_small<NTV>, grid, block, 0, stream, dy, M, N, K, packed, qscale, step, S, part, B, r, \
                      rp, upart, cb)
+  mark_kernel(0, stream);
   if (nt == 0)
     QNF4_BWDS(0);
   else if (nt == 1)
@@ -240,6 +241,7 @@ hipError_t launch_bwd_small(const uint16_t* dy, int64_t M, int64_t N, int64_t K,
   else
     QNF4_BWDS(8);
 #undef QNF4_BWDS
+  mark_kernel(1, stream);
   hipLaunchKernelGGL(k_bwd_finish, dim3(static_cast<unsigned>(cdiv(K, 256)), static_cast<unsigned>(M)), dim3(256),
                      0, stream, part, S, M, K, upart, S, rp, A, r, scale, dx);
   return hipGetLastError();

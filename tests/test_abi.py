@@ -39,6 +39,13 @@ def test_abi_version_and_status_strings():
     assert L.qlora_status_string(99) == b"unknown status"
 
 
+def test_kernel_events_setting():
+    L = _lib.lib()
+    assert L.qlora_set_kernel_events(FAKE, V(0)) == 1
+    assert L.qlora_set_kernel_events(V(0), FAKE) == 1
+    assert L.qlora_set_kernel_events(V(0), V(0)) == 0
+
+
 def test_codebook_bitwise_equals_oracle():
     levels, thresholds = ops.codebook()
     L = np.array(levels, np.float32)
