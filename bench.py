@@ -244,6 +244,11 @@ class StackWorkload:
                 torch.cuda.synchronize()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 with torch.cuda.stream(qstream):
+                    # keep the stream busy while the host issues the launch, so
+                    # that the events bracket the kernel and not the host's
+                    # argument checks and launch latency
+                    if hasattr(torch.cuda, "_sleep"):
+                        torch.cuda._sleep(2_000_000)
                     e0.record(qstream)
                     ops.quantize_dq(w, packed=packed, absmax=absmax, q=q, step=st)
                     e1.record(qstream)
