@@ -7,7 +7,7 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libqlora_nf4.so")
+LIB_PATH = os.environ.get("QLORA_NF4_LIB") or os.path.join(HERE, "libqlora_nf4.so")
 
 QLORA_OK = 0
 STATUS = {0: "QLORA_OK", 1: "QLORA_ERR_NULL", 2: "QLORA_ERR_SHAPE", 3: "QLORA_ERR_ALIGN",

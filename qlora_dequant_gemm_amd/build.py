@@ -64,5 +64,47 @@ def build(verbose=False, extra=()):
     return LIB
 
 
+# Host-side sanitizer build of the C ABI layer (argument checks, codebook
+# derivation, dispatch): api.cpp and codebook.cpp with AddressSanitizer and
+# UndefinedBehaviorSanitizer on their host code only, linked with the regular
+# kernel objects into a separate library for the CPU ABI tests (run with the
+# sanitizer runtime preloaded; nothing here is used by the product path).
+SAN_SOURCES = ["codebook.cpp", "api.cpp"]
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
+SAN_LIB = os.path.join(OBJ, "san", "libqlora_nf4_san.so")
+
+
+def build_sanitized(verbose=False):
+    if not all(os.path.exists(os.path.join(OBJ, os.path.splitext(s)[0] + ".o")) for s in SOURCES):
+        build(verbose)
+    san = os.path.dirname(SAN_LIB)
+    os.makedirs(san, exist_ok=True)
+    objs = []
+    for s in SOURCES:
+        if s in SAN_SOURCES:
+            obj = os.path.join(san, os.path.splitext(s)[0] + ".o")
+            if _run([hipcc()] + FLAGS + SAN_FLAGS + ["-c", os.path.join(CSRC, s), "-o", obj], verbose):
+                raise RuntimeError("hipcc failed building the sanitizer objects")
+        else:
+            obj = os.path.join(OBJ, os.path.splitext(s)[0] + ".o")
+        objs.append(obj)
+    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libsan"] + SAN_FLAGS + ["-o", SAN_LIB] + objs
+    if _run(link, verbose):
+        raise RuntimeError("hipcc failed linking the sanitizer library")
+    return SAN_LIB
+
+
+def sanitizer_runtime():
+    """The AddressSanitizer runtime the sanitizer library expects preloaded."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    clang = os.path.join(rocm, "llvm", "bin", "clang")
+    res = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return res.stdout.strip()
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if "--sanitize" in sys.argv:
+        print(build_sanitized(verbose=True))
+    else:
+        print(build(verbose=True))
