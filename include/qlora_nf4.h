@@ -199,10 +199,13 @@ int qlora_nf4_lora_fwd_noalloc(const uint16_t* x, int64_t M, int64_t N,
  *     y[i] = bf16( x . W_i'^T + (alpha / r) . (x . A_i^T) . B_i^T )
  * For M <= 16 the weights are streamed by one launch of the decode-shaped
  * kernel (qlora_nf4_lora_fwd_batched with x repeated), so the launch ramp is
- * paid once; larger M runs the tiled forward per weight. The decode kernel
- * chooses its split of K from the whole group, so results can differ from
- * the single calls in the fp32 summation order (both within the tolerance of
- * the single call; repeated identical calls are bitwise identical).
+ * paid once; the decode kernel chooses its split of K from the whole group,
+ * so results can differ from the single calls in the fp32 summation order
+ * (both within the tolerance of the single call; repeated identical calls are
+ * bitwise identical). Larger M runs one LoRA down-projection per weight and
+ * then one tiled GEMM launch for all G weights, whose tile order sweeps each
+ * group of x rows across every weight (x is read from HBM once for the group);
+ * its outputs are bitwise those of the single calls.
  *   x        [M, K] bf16 (device); G in 1..8.
  *   packed, qscale, step, N, A, B, y  host arrays of G entries: the device
  *            pointers of weight i's stored format (N[i] rows), its adapters
@@ -240,7 +243,8 @@ int qlora_nf4_lora_fwd_grouped(const uint16_t* x, int64_t M, int64_t K, int G,
  *            r) bytes, with the same zero-counter rule as every workspace
  *            (below).
  * M <= 16 runs the decode-shaped kernel over the whole table; larger M runs
- * the tiled forward weight by weight.
+ * the tiled forward, one GEMM launch per 8 weights (after each weight's LoRA
+ * down-projection), with results bitwise those of the single calls.
  */
 #define QLORA_MAX_BATCH 4096
 int qlora_nf4_lora_fwd_batched(int G, int64_t M, const uint16_t* const* x,

@@ -102,13 +102,8 @@ struct BScale4 {   // the same for the four steps of a super-step
 // loaded once per super-step. Otherwise they are loaded per step.
 // RSN: rank_pad(r) / 16 (chunks of 16 ranks in the LoRA epilogue), 0 for none.
 template <bool kQuad, int RSN>
-__global__ __launch_bounds__(256, 1) void k_gemm_fwd(const uint16_t* __restrict__ x, int64_t M, int64_t N,
-                                                     int64_t K, const uint8_t* __restrict__ packed,
-                                                     const int8_t* __restrict__ qscale,
-                                                     const float* __restrict__ step,
-                                                     const uint16_t* __restrict__ tl, int rp,
-                                                     const uint16_t* __restrict__ Bl, int r, float scale,
-                                                     uint16_t* __restrict__ y, Codebook cb) {
+__global__ __launch_bounds__(256, 1) void k_gemm_fwd(FwdTable tab, int64_t M, int rp, int r, float scale,
+                                                     Codebook cb) {
   // ring of four x tiles (32 KB each) and the per-wave code slabs (8 KB each),
   // distinct objects so that the compiler can tell a DMA into one from reads
   // of another
@@ -120,11 +115,28 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd(const uint16_t* __restrict_
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave index, provably uniform (SGPR)
   const int h = lane >> 5, l32 = lane & 31;
-  const int ntm = static_cast<int>(cdiv(M, kTile)), ntn = static_cast<int>(cdiv(N, kTile));
-  int tm, tn;
-  tile_of(blockIdx.x, ntm, ntn, tm, tn);
+  // The weights' tile columns are numbered one after another, so the tile
+  // order sweeps groups of tile-rows across every weight of the table (x
+  // rows shared by weights with the same input stay in L2 across them).
+  const int ntm = static_cast<int>(cdiv(M, kTile));
+  int tm, tnv;
+  tile_of(blockIdx.x, ntm, tab.col0[tab.count], tm, tnv);
   tm = __builtin_amdgcn_readfirstlane(tm);     // uniform already; this keeps the
-  tn = __builtin_amdgcn_readfirstlane(tn);     // buffer descriptors in SGPRs
+  tnv = __builtin_amdgcn_readfirstlane(tnv);   // buffer descriptors in SGPRs
+  int g = 0;
+#pragma unroll
+  for (int i = 1; i < kFwdMaxWeights; ++i)
+    if (i < tab.count && tnv >= tab.col0[i]) g = i;
+  g = __builtin_amdgcn_readfirstlane(g);
+  const int tn = tnv - tab.col0[g];
+  const uint16_t* __restrict__ x = tab.x[g];
+  const uint8_t* __restrict__ packed = tab.packed[g];
+  const int8_t* __restrict__ qscale = tab.qscale[g];
+  const float* __restrict__ step = tab.step[g];
+  const uint16_t* __restrict__ tl = tab.tl[g];
+  const uint16_t* __restrict__ Bl = tab.B[g];
+  uint16_t* __restrict__ y = tab.y[g];
+  const int64_t N = tab.N[g], K = tab.K[g];
   const int64_t m0 = static_cast<int64_t>(tm) * kTile, n0 = static_cast<int64_t>(tn) * kTile;
   const int64_t nk = K / 64;
   const int64_t nsup = (nk + 3) / 4;           // super-steps of four K steps
@@ -743,34 +755,53 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd(const uint16_t* __restrict_
 // ---------------------------------------------------------------------------
 // dispatch: LoRA down-projection, then the small-M or the tiled kernel
 // ---------------------------------------------------------------------------
-hipError_t launch_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
-                           const int8_t* qscale, const float* step, const uint16_t* A, const uint16_t* B,
-                           int r, float alpha, uint16_t* y, void* ws, const Codebook& cb,
-                           hipStream_t stream) {
-  if (M <= kSmallM)
-    return launch_dec_fwd(M, 1, &x, &N, &K, &packed, &qscale, &step, &A, &B, r, alpha, &y, ws, cb, stream);
-  const WsLayout L = ws_layout(0, M, N, K, r);
-  char* wsb = static_cast<char*>(ws);
+// The tiled forward over a table of up to kFwdMaxWeights weights at one M:
+// the LoRA down-projection of each weight into its own workspace slice (one
+// launch each), then one launch of k_gemm_fwd for all of them. Weight i's
+// workspace is ws + i * ws_stride (its layout ws_layout(0, M, N[i], K[i], r)).
+static hipError_t launch_fwd_tiled(int64_t M, int G, const uint16_t* const* x, const int64_t* N, const int64_t* K,
+                                   const uint8_t* const* packed, const int8_t* const* qscale,
+                                   const float* const* step, const uint16_t* const* A, const uint16_t* const* B,
+                                   int r, float alpha, uint16_t* const* y, void* ws, size_t ws_stride,
+                                   const Codebook& cb, hipStream_t stream) {
   const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
   const int rp = r > 0 ? static_cast<int>(rank_pad(r)) : 0;
-  void* lora = r > 0 ? static_cast<void*>(wsb + L.lora_off) : nullptr;
-  if (r > 0) {
-    const hipError_t e = launch_lora_down(true, x, M, K, A, r, lora, stream, nullptr,
-                                          reinterpret_cast<float*>(wsb + L.dp_off));
-    if (e != hipSuccess) return e;
+  FwdTable tab{};
+  tab.count = G;
+  bool quad = true;
+  int cols = 0;
+  for (int i = 0; i < G; ++i) {
+    const WsLayout L = ws_layout(0, M, N[i], K[i], r);
+    char* wsb = static_cast<char*>(ws) + static_cast<size_t>(i) * ws_stride;
+    void* lora = r > 0 ? static_cast<void*>(wsb + L.lora_off) : nullptr;
+    if (r > 0) {
+      const hipError_t e = launch_lora_down(true, x[i], M, K[i], A[i], r, lora, stream, nullptr,
+                                            reinterpret_cast<float*>(wsb + L.dp_off));
+      if (e != hipSuccess) return e;
+    }
+    tab.x[i] = x[i];
+    tab.packed[i] = packed[i];
+    tab.qscale[i] = qscale[i];
+    tab.step[i] = step[i];
+    tab.tl[i] = static_cast<const uint16_t*>(lora);
+    tab.B[i] = r > 0 ? B[i] : nullptr;
+    tab.y[i] = y[i];
+    tab.N[i] = static_cast<int>(N[i]);
+    tab.K[i] = static_cast<int>(K[i]);
+    tab.col0[i] = cols;
+    cols += static_cast<int>(cdiv(N[i], kTile));
+    quad = quad && K[i] % 256 == 0;
   }
-  const int64_t tiles = cdiv(M, kTile) * cdiv(N, kTile);
-  const bool quad = K % 256 == 0;
+  tab.col0[G] = cols;
+  const int64_t tiles = cdiv(M, kTile) * cols;
 #define QNF4_FWD(RSNV)                                                                                          \
   do {                                                                                                         \
     if (quad)                                                                                                  \
       hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_fwd<true, RSNV>), dim3(static_cast<unsigned>(tiles)), dim3(256), \
-                         0, stream, x, M, N, K, packed, qscale, step, static_cast<const uint16_t*>(lora), rp, B, \
-                         r, scale, y, cb);                                                                     \
+                         0, stream, tab, M, rp, r, scale, cb);                                                 \
     else                                                                                                       \
       hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_fwd<false, RSNV>), dim3(static_cast<unsigned>(tiles)),          \
-                         dim3(256), 0, stream, x, M, N, K, packed, qscale, step,                               \
-                         static_cast<const uint16_t*>(lora), rp, B, r, scale, y, cb);                          \
+                         dim3(256), 0, stream, tab, M, rp, r, scale, cb);                                      \
   } while (0)
   mark_kernel(0, stream);
   switch (rp / 16) {
@@ -785,14 +816,30 @@ hipError_t launch_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K, c
   return hipGetLastError();
 }
 
-size_t batched_ws_bytes(int64_t M, int G, const int64_t* N, const int64_t* K, int r) {
-  if (M <= kSmallM) return dec_workspace_bytes(M, G, N, K);
+hipError_t launch_lora_fwd(const uint16_t* x, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
+                           const int8_t* qscale, const float* step, const uint16_t* A, const uint16_t* B,
+                           int r, float alpha, uint16_t* y, void* ws, const Codebook& cb,
+                           hipStream_t stream) {
+  if (M <= kSmallM)
+    return launch_dec_fwd(M, 1, &x, &N, &K, &packed, &qscale, &step, &A, &B, r, alpha, &y, ws, cb, stream);
+  return launch_fwd_tiled(M, 1, &x, &N, &K, &packed, &qscale, &step, &A, &B, r, alpha, &y, ws, 0, cb, stream);
+}
+
+// Tiled batches go in chunks of kFwdMaxWeights, each weight with a workspace
+// slice of the largest single-weight size in the batch.
+static size_t tiled_stride(int64_t M, int G, const int64_t* N, const int64_t* K, int r) {
   size_t need = 0;
   for (int i = 0; i < G; ++i) {
-    const size_t b = ws_layout(0, M, N[i], K[i], r).total;
+    const size_t b = align256(ws_layout(0, M, N[i], K[i], r).total);
     need = b > need ? b : need;
   }
   return need;
+}
+
+size_t batched_ws_bytes(int64_t M, int G, const int64_t* N, const int64_t* K, int r) {
+  if (M <= kSmallM) return dec_workspace_bytes(M, G, N, K);
+  const int per_launch = G < kFwdMaxWeights ? G : kFwdMaxWeights;
+  return tiled_stride(M, G, N, K, r) * static_cast<size_t>(per_launch);
 }
 
 hipError_t launch_lora_fwd_batched(int64_t M, int G, const uint16_t* const* x, const int64_t* N, const int64_t* K,
@@ -801,9 +848,12 @@ hipError_t launch_lora_fwd_batched(int64_t M, int G, const uint16_t* const* x, c
                                    int r, float alpha, uint16_t* const* y, void* ws, const Codebook& cb,
                                    hipStream_t stream) {
   if (M <= kSmallM) return launch_dec_fwd(M, G, x, N, K, packed, qscale, step, A, B, r, alpha, y, ws, cb, stream);
-  for (int i = 0; i < G; ++i) {
-    const hipError_t e = launch_lora_fwd(x[i], M, N[i], K[i], packed[i], qscale[i], step[i], r ? A[i] : nullptr,
-                                         r ? B[i] : nullptr, r, alpha, y[i], ws, cb, stream);
+  const size_t stride = tiled_stride(M, G, N, K, r);
+  for (int c0 = 0; c0 < G; c0 += kFwdMaxWeights) {
+    const int cn = G - c0 < kFwdMaxWeights ? G - c0 : kFwdMaxWeights;
+    const hipError_t e = launch_fwd_tiled(M, cn, x + c0, N + c0, K + c0, packed + c0, qscale + c0, step + c0,
+                                          r ? A + c0 : nullptr, r ? B + c0 : nullptr, r, alpha, y + c0, ws, stride,
+                                          cb, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

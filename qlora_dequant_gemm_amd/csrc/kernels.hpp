@@ -35,6 +35,22 @@ constexpr int kDecMaxProblems = 32;
 constexpr int kMaxGroups = 8;             // weights of one grouped (shared-x) forward
 constexpr int64_t kDecTargetItems = 1024;
 
+// Tiled forward (M > kSmallM) over a table of weights in one launch; tile
+// columns of weight i are [col0[i], col0[i + 1]) of the launch's sequence.
+constexpr int kFwdMaxWeights = 8;
+struct FwdTable {
+  const uint16_t* x[kFwdMaxWeights];        // [M][K[i]]
+  const uint8_t* packed[kFwdMaxWeights];
+  const int8_t* qscale[kFwdMaxWeights];
+  const float* step[kFwdMaxWeights];
+  const uint16_t* tl[kFwdMaxWeights];       // t = bf16(x . A^T) [M][rp], or null
+  const uint16_t* B[kFwdMaxWeights];        // [N[i]][r], or null
+  uint16_t* y[kFwdMaxWeights];              // [M][N[i]]
+  int N[kFwdMaxWeights], K[kFwdMaxWeights];
+  int col0[kFwdMaxWeights + 1];
+  int count;
+};
+
 struct DecFwdProblem {
   const uint16_t* x;        // [M][K]
   const uint8_t* packed;    // stored weight [N][K]

@@ -112,8 +112,13 @@ def test_workspace_sizes():
     K = (ctypes.c_int64 * 3)(4096, 4096, 11008)
     b = _lib.lib().qlora_workspace_bytes_batched(3, 16, N, K, 16)
     assert b >= C and (b - C) % (16 * 256 * 4) == 0
-    assert _lib.lib().qlora_workspace_bytes_batched(3, 4096, N, K, 16) == max(ws(0, 4096, n, k, 16)
-                                                                               for n, k in zip(N, K))
+    # training shapes: one launch per 8 weights, each with its own slice of
+    # the largest single-weight size
+    assert _lib.lib().qlora_workspace_bytes_batched(3, 4096, N, K, 16) == 3 * max(ws(0, 4096, n, k, 16)
+                                                                                   for n, k in zip(N, K))
+    N12 = (ctypes.c_int64 * 12)(*([4096] * 12))
+    K12 = (ctypes.c_int64 * 12)(*([4096] * 12))
+    assert _lib.lib().qlora_workspace_bytes_batched(12, 4096, N12, K12, 16) == 8 * ws(0, 4096, 4096, 4096, 16)
     assert _lib.lib().qlora_workspace_bytes_batched(0, 16, N, K, 16) == 0
 
 

@@ -793,7 +793,9 @@ def test_decode_backward_every_output_vs_oracle(qops, name, M):
 
 @pytest.mark.parametrize("M,r,Ns,K", [(1, 16, [512, 200, 64], 512), (16, 16, [4096, 4096, 4096], 4096),
                                       (4, 0, [11008, 11008], 4096), (40, 16, [300, 520], 320),
-                                      (7, 32, [64, 136, 8, 1000, 72, 96, 520, 264], 768)])
+                                      (7, 32, [64, 136, 8, 1000, 72, 96, 520, 264], 768),
+                                      (300, 16, [4096, 1000, 264, 8], 320), (513, 32, [520, 264, 72], 576),
+                                      (257, 0, [600, 300], 1024)])
 def test_grouped_forward_vs_oracle(qops, M, r, Ns, K):
     """Each output of the grouped forward against the oracle, element-wise."""
     alpha = 32.0
@@ -818,15 +820,36 @@ def test_grouped_forward_vs_oracle(qops, M, r, Ns, K):
         assert rel_fro(got, ref) <= TIGHT, i
 
 
+def test_grouped_tiled_bitwise_equals_single_calls(qops):
+    """At training shapes the grouped forward is one GEMM launch over all the
+    weights; each output is bitwise the single call's (same tiles, same
+    order of summation), also for a K that is not a multiple of 256."""
+    for M, K, Ns in ((300, 1024, [1000, 264, 4096]), (520, 576, [520, 64])):
+        r, alpha = 16, 32.0
+        x = dev(synth.activations(M, K, 2100 + M))
+        qws, As, Bs = [], [], []
+        for i, N in enumerate(Ns):
+            qws.append(gpu_quant(qops, synth.weight(N, K, 2110 + i)))
+            A, B = synth.adapters(N, K, r, 2120 + i, 2130 + i)
+            As.append(dev(A))
+            Bs.append(dev(B))
+        outs = qops.lora_fwd_grouped(x, qws, As, Bs, alpha)
+        for i in range(len(Ns)):
+            single = qops.lora_fwd(x, qws[i], As[i], Bs[i], alpha)
+            assert np.array_equal(host_bits(outs[i]), host_bits(single)), (M, K, i)
+
+
 # ---------------------------------------------------------------------------
 # batched forward: independent inputs and shapes per weight in one call
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("M,r,G,seed", [(1, 16, 5, 0), (16, 16, 7, 1), (4, 0, 3, 2), (3, 5, 4, 3),
-                                        (16, 64, 3, 4), (8, 128, 2, 5), (2, 32, 40, 6), (40, 16, 3, 7)])
+                                        (16, 64, 3, 4), (8, 128, 2, 5), (2, 32, 40, 6), (40, 16, 3, 7),
+                                        (40, 16, 11, 8)])
 def test_batched_forward_vs_oracle(qops, M, r, G, seed):
     """Weights of mixed shapes (K = 64 .. 11008, ragged N), each with its own
     x: every output against the oracle element-wise. G = 40 spans two
-    launches (32 weights per launch); M = 40 takes the tiled path."""
+    launches (32 weights per launch); M = 40 takes the tiled path (one GEMM
+    launch per 8 weights: G = 11 spans two)."""
     rng = np.random.Generator(np.random.PCG64(3000 + seed))
     shapes = [(int(rng.choice([8, 64, 136, 520, 1000, 4096])), int(rng.choice([64, 320, 1024, 4096, 11008])))
               for _ in range(G)]
