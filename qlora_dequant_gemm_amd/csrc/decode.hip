@@ -462,10 +462,10 @@ DecChunkPlan dec_plan_chunk(int64_t M, int cn, const int64_t* N, const int64_t* 
   DecChunkPlan pl;
   int64_t rb_total = 0;
   for (int i = 0; i < cn; ++i) rb_total += cdiv(N[i], kDecRows);
-  // about kDecTargetItems items per launch; at M > 4 a split covers at least
-  // two super-steps (its fp32 partials are M KB per 256 rows)
+  // about kDecTargetItems items per launch; a split covers at least two
+  // super-steps (each split costs a round of fp32 partials and a fix-up)
   const int64_t s_all = rb_total >= kDecTargetItems / 2 ? 1 : cdiv(kDecTargetItems, rb_total);
-  const int64_t min_sps = M > 4 ? 2 : 1;
+  const int64_t min_sps = 2;
   for (int i = 0; i < cn; ++i) {
     const int64_t nss = cdiv(K[i] / 64, 4);
     int64_t S = s_all < nss ? s_all : nss;

@@ -93,7 +93,7 @@ def test_workspace_sizes():
     # decode shapes: 16 row blocks of 256 x 8 splits of K (two 256-deep steps
     # each at M = 16) of fp32 partials [M][256]; one split needs nothing
     assert ws(0, 16, 4096, 4096, 16) == C + 16 * 8 * 16 * 256 * 4
-    assert ws(0, 1, 4096, 4096, 16) == C + 16 * 16 * 1 * 256 * 4
+    assert ws(0, 1, 4096, 4096, 16) == C + 16 * 8 * 1 * 256 * 4
     assert ws(0, 16, 8, 64, 8) == 0
     assert ws(1, 16, 4096, 4096, 0) > 0                           # small-M backward partials
     assert ws(1, 4096, 4096, 11008, 0) == 0
