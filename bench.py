@@ -372,6 +372,17 @@ class StackWorkload:
                                                             out=self.dxd[(M, K)], ws=ws))
         return fns
 
+    def decode_bwd_batched(self, M):
+        """All 224 backward dX at M tokens as one batched call (one launch
+        per 32 weights; the linears of this synthetic stack do not depend on
+        one another)."""
+        ops, a, ws = self.ops, self.alpha, self.ws
+        ds = [d for row in self.lay for d in row]
+        dys = [self.dyd[(M, self.lin[j][1])] for _ in range(self.L) for j in range(len(self.lin))]
+        outs = [self.dxd[(M, self.lin[j][2])] for _ in range(self.L) for j in range(len(self.lin))]
+        return [lambda: ops.bwd_dx_batched(dys, [d["qw"] for d in ds], [d["A"] for d in ds],
+                                           [d["B"] for d in ds], a, outs=outs, ws=ws)]
+
     def walk_bytes(self, M):
         """Algorithmic bytes of one walk: every weight's stored format and
         adapters once, plus each call's activations in and out."""
@@ -527,6 +538,13 @@ def decode_walks(wl, stream, reps=10):
                         "hbm_frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4), "bytes": b,
                         "launch_groups": len(wl.lin) * wl.L}
     print(f"# decode bwd walk M={M}: {ms:.4f} ms", file=sys.stderr, flush=True)
+    g = graph_of(wl.decode_bwd_batched(M), stream)
+    ms = time_graph(g, stream, reps)
+    del g
+    out[f"bwd_batched_M{M}"] = {"ms": round(ms, 4), "GB/s": round(b / ms / 1e6, 1),
+                                "hbm_frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4), "bytes": b,
+                                "launches": -(-len(wl.lin) * wl.L // 32)}
+    print(f"# decode bwd batched M={M}: {ms:.4f} ms, {b / ms / 1e6:.1f} GB/s", file=sys.stderr, flush=True)
     return out
 
 
@@ -886,8 +904,10 @@ def main():
                                         "grouped call), o, gate/up (one grouped call), down -- 128 dependent "
                                         "launches; fwd_batched_M: all 224 linears in one batched call (7 "
                                         "launches; the synthetic linears are independent). bytes = every "
-                                        "weight's stored format + adapters + activations once; bwd = backward "
-                                        "dX of all 224 linears at M = 16")
+                                        "weight's stored format + adapters + activations once; bwd_M16: the "
+                                        "backward dX of all 224 linears at M = 16, one call each in reverse "
+                                        "layer order (224 dependent launches); bwd_batched_M16: the same as "
+                                        "one batched call (7 launches)")
         line["roofline_decode"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                    "frac": round(ach / HBM_PEAK_GBS, 4), "kernel": "k_dec_fwd",
                                    "traffic": read_traffic("k_dec_fwd", "decode.hip", "7b_stack_decode"),

@@ -279,6 +279,41 @@ int qlora_nf4_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K,
                      size_t ws_bytes, void* stream);
 
 /*
+ * Backward dX of G independent QLoRA linears in as few launches as possible
+ * (decode shapes: one launch per 32 weights, streaming all of them), e.g. the
+ * linears of a model whose backward inputs are all at hand, or many small
+ * requests against different weights. For each i:
+ *     dx[i] = bf16( dy[i] . W_i' + (alpha / r) . u_i . A[i] ),
+ *     u_i = dy[i] . B[i]
+ *   dy, packed, qscale, step, N, K, A, B, dx  host arrays of G entries (G in
+ *            1..QLORA_MAX_BATCH): the device pointers of weight i's operands,
+ *            its sizes (N[i] >= 1 multiple of 8, K[i] multiple of 64) and its
+ *            output dx[i] [M, K[i]]; one M and one rank r for all (A and B
+ *            may be NULL with r = 0).
+ *   workspace / ws_bytes  at least qlora_workspace_bytes_bwd_batched(G, M, N,
+ *            K, r) bytes, with the zero-counter rule of every workspace.
+ * M <= 16 runs the decode-shaped backward over the whole table, which carries
+ * u_i as the sum of two bf16 values (about 16 significant bits) when it
+ * splits a weight's rows; larger M runs the single call per weight. Results
+ * equal the single calls' (within their tolerance) and repeated identical
+ * calls are bitwise identical. Alignment and size limits as in
+ * qlora_nf4_bwd_dx.
+ */
+int qlora_nf4_bwd_dx_batched(int G, int64_t M, const uint16_t* const* dy,
+                             const int64_t* N, const int64_t* K,
+                             const uint8_t* const* packed,
+                             const int8_t* const* qscale,
+                             const float* const* step,
+                             const uint16_t* const* A,
+                             const uint16_t* const* B, int r, float alpha,
+                             uint16_t* const* dx, void* workspace,
+                             size_t ws_bytes, void* stream);
+
+/* Workspace bytes qlora_nf4_bwd_dx_batched needs (0 for invalid sizes). */
+size_t qlora_workspace_bytes_bwd_batched(int G, int64_t M, const int64_t* N,
+                                         const int64_t* K, int r);
+
+/*
  * Gradients of the LoRA adapters of one QLoRA linear, the only trainable
  * parameters: the base weight is frozen and gradients and optimizer state
  * exist for the adapters alone ("QLoRA Explained", "What is QLoRA?"; "QLoRA

@@ -36,6 +36,9 @@ SIGNATURES = [
     ("qlora_workspace_bytes_batched", _sz, [_i32, _i64, _vp, _vp, _i32]),
     ("qlora_nf4_bwd_dx", _i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _f32,
                                 _vp, _vp, _sz, _vp]),
+    ("qlora_nf4_bwd_dx_batched", _i32, [_i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _f32,
+                                        _vp, _vp, _sz, _vp]),
+    ("qlora_workspace_bytes_bwd_batched", _sz, [_i32, _i64, _vp, _vp, _i32]),
     ("qlora_q4_quantize", _i32, [_vp, _i32, _i64, _i32, _vp, _vp, _vp, _vp, _vp]),
     ("qlora_q4_dequant", _i32, [_vp, _vp, _vp, _vp, _i64, _i32, _vp, _vp]),
     ("qlora_q4_codebook", _i32, [_i32, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float)]),

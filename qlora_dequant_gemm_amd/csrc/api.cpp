@@ -290,6 +290,38 @@ int qlora_nf4_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K, const 
                                         as_stream(stream)));
 }
 
+size_t qlora_workspace_bytes_bwd_batched(int G, int64_t M, const int64_t* N, const int64_t* K, int r) {
+  if (G < 1 || G > QLORA_MAX_BATCH || !N || !K || r < 0 || r > QLORA_MAX_RANK) return 0;
+  for (int i = 0; i < G; ++i)
+    if (N[i] % 8 != 0 || check_mm(M, N[i], K[i])) return 0;
+  return qnf4::bwd_batched_ws_bytes(M, G, N, K, r);
+}
+
+int qlora_nf4_bwd_dx_batched(int G, int64_t M, const uint16_t* const* dy, const int64_t* N, const int64_t* K,
+                             const uint8_t* const* packed, const int8_t* const* qscale, const float* const* step,
+                             const uint16_t* const* A, const uint16_t* const* B, int r, float alpha,
+                             uint16_t* const* dx, void* workspace, size_t ws_bytes, void* stream) {
+  if (!dy || !N || !K || !packed || !qscale || !step || !dx) return QLORA_ERR_NULL;
+  if (G < 1 || G > QLORA_MAX_BATCH) return QLORA_ERR_SHAPE;
+  if (r < 0 || r > QLORA_MAX_RANK) return QLORA_ERR_RANK;
+  if (r > 0 && (!A || !B)) return QLORA_ERR_NULL;
+  for (int i = 0; i < G; ++i) {
+    int st = check_weight(packed[i], qscale[i], step[i]);
+    if (st) return st;
+    if (!dy[i] || !dx[i]) return QLORA_ERR_NULL;
+    if (N[i] % 8 != 0 || check_mm(M, N[i], K[i])) return QLORA_ERR_SHAPE;
+    if (!aligned16(dy[i]) || !aligned16(dx[i])) return QLORA_ERR_ALIGN;
+    st = check_adapter(r ? A[i] : nullptr, r ? B[i] : nullptr, r);
+    if (st) return st;
+  }
+  const int st = check_ws(workspace, ws_bytes, qnf4::bwd_batched_ws_bytes(M, G, N, K, r));
+  if (st) return st;
+  const qnf4::Codebook* cb = qnf4::codebook();
+  if (!cb) return QLORA_ERR_INIT;
+  return hip_status(qnf4::launch_bwd_dx_batched(M, G, dy, N, K, packed, qscale, step, A, B, r, alpha, dx, workspace,
+                                                *cb, as_stream(stream)));
+}
+
 int qlora_q4_quantize(const void* w, int wdt, int64_t numel, int format, uint8_t* packed, float* absmax,
                       int8_t* qscale, float* step, void* stream) {
   if (!w || !packed || !absmax) return QLORA_ERR_NULL;

@@ -53,16 +53,6 @@
 
 namespace qnf4 {
 
-// 8 consecutive bf16 (4 dwords, low half first) -> the order 0 2 | 4 6 | 1 3 | 5 7
-__device__ __forceinline__ u32x4 perm8(const u32x4& v) {
-  u32x4 r;
-  r.x = perm(v.y, v.x, 0x05040100u);
-  r.y = perm(v.w, v.z, 0x05040100u);
-  r.z = perm(v.y, v.x, 0x07060302u);
-  r.w = perm(v.w, v.z, 0x07060302u);
-  return r;
-}
-
 constexpr int kDecNT = 4;                         // 16-row MFMA tiles per wave
 constexpr int kDecBufWord3 = 0x00020000;          // raw buffer descriptor word 3 on gfx9-family parts
 constexpr int kDecRows = 16 * kDecNT * 4;         // weight rows per item (four waves)

@@ -121,6 +121,16 @@ __device__ __forceinline__ u32x4 decode8_perm(uint32_t d, const MagTable& t) {
   return r;
 }
 
+// 8 consecutive bf16 (4 dwords, low half first) -> the order 0 2 | 4 6 | 1 3 | 5 7
+__device__ __forceinline__ u32x4 perm8(const u32x4& v) {
+  u32x4 r;
+  r.x = perm(v.y, v.x, 0x05040100u);
+  r.y = perm(v.w, v.z, 0x05040100u);
+  r.z = perm(v.y, v.x, 0x07060302u);
+  r.w = perm(v.w, v.z, 0x07060302u);
+  return r;
+}
+
 // Block scale s = fp32(q * d) of the double-quantized constants.
 __device__ __forceinline__ float block_scale(int8_t q, float d) {
   return static_cast<float>(q) * d;

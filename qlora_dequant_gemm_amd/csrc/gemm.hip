@@ -865,15 +865,14 @@ hipError_t launch_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K, co
                          const int8_t* qscale, const float* step, const uint16_t* A, const uint16_t* B,
                          int r, float alpha, uint16_t* dx, void* ws, const Codebook& cb,
                          hipStream_t stream) {
+  // small M: the down-projection u = dY . B is computed inside k_dec_bwd
+  if (M <= kSmallM)
+    return launch_dec_bwd(M, 1, &dy, &N, &K, &packed, &qscale, &step, &A, &B, r, alpha, &dx, ws, cb, stream);
   const WsLayout L = ws_layout(1, M, N, K, r);
   char* wsb = static_cast<char*>(ws);
   const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
   const int rp = r > 0 ? static_cast<int>(rank_pad(r)) : 0;
   void* lora = r > 0 ? static_cast<void*>(wsb + L.lora_off) : nullptr;
-  // small M: the down-projection u = dY . B is computed inside k_bwd_small
-  if (M <= kSmallM)
-    return launch_bwd_small(dy, M, N, K, packed, qscale, step, static_cast<float*>(lora), rp, A, B, r, scale,
-                            reinterpret_cast<float*>(wsb + L.part_off), dx, cb, stream);
   if (r > 0) {
     const hipError_t e = launch_lora_down(false, dy, M, N, B, r, lora, stream,
                                           reinterpret_cast<uint16_t*>(wsb + L.bt_off),
@@ -895,6 +894,30 @@ hipError_t launch_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K, co
 #undef QNF4_BWD
   mark_kernel(1, stream);
   return hipGetLastError();
+}
+
+size_t bwd_batched_ws_bytes(int64_t M, int G, const int64_t* N, const int64_t* K, int r) {
+  if (M <= kSmallM) return dec_bwd_workspace_bytes(M, G, N, K);
+  size_t most = 0;                           // the tiled calls run one after another on one workspace
+  for (int i = 0; i < G; ++i) {
+    const size_t b = ws_layout(1, M, N[i], K[i], r).total;
+    if (b > most) most = b;
+  }
+  return most;
+}
+
+hipError_t launch_bwd_dx_batched(int64_t M, int G, const uint16_t* const* dy, const int64_t* N, const int64_t* K,
+                                 const uint8_t* const* packed, const int8_t* const* qscale,
+                                 const float* const* step, const uint16_t* const* A, const uint16_t* const* B,
+                                 int r, float alpha, uint16_t* const* dx, void* ws, const Codebook& cb,
+                                 hipStream_t stream) {
+  if (M <= kSmallM) return launch_dec_bwd(M, G, dy, N, K, packed, qscale, step, A, B, r, alpha, dx, ws, cb, stream);
+  for (int i = 0; i < G; ++i) {
+    const hipError_t e = launch_bwd_dx(dy[i], M, N[i], K[i], packed[i], qscale[i], step[i], r ? A[i] : nullptr,
+                                       r ? B[i] : nullptr, r, alpha, dx[i], ws, cb, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace qnf4

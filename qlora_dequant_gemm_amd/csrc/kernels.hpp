@@ -84,16 +84,36 @@ hipError_t launch_dec_fwd(int64_t M, int G, const uint16_t* const* x, const int6
                           const uint16_t* const* A, const uint16_t* const* B, int r, float alpha,
                           uint16_t* const* y, void* ws, const Codebook& cb, hipStream_t stream);
 
-// Row slices of the small-M backward (fp32 partials of dX): enough column
-// tiles x slices for about one workgroup per CU, 1024 weight rows per step.
-inline int64_t bwd_small_splits(int64_t N, int64_t K) {
-  const int64_t ktiles = cdiv(K, 64);
-  int64_t s = cdiv(256, ktiles);
-  const int64_t steps = cdiv(N, 1024);
-  if (s > steps) s = steps;
-  if (s < 1) s = 1;
-  return s;
-}
+// Decode-shaped backward (M <= kSmallM) over a table of weights, one launch
+// per chunk of kDecMaxProblems: items are 64-column block columns of dX x S_p
+// ranges of the weight's rows (64-row sub-tiles, at least kDbMinSps per range).
+constexpr int64_t kDbMinSps = 8;
+constexpr int64_t kDbTargetItems = 1024;
+struct DecBwdProblem {
+  const uint16_t* dy;       // [M][N]
+  const uint8_t* packed;    // stored weight [N][K]
+  const int8_t* qscale;
+  const float* step;
+  const uint16_t* A;        // [r][K] (r > 0)
+  const uint16_t* B;        // [N][r]
+  uint16_t* dx;             // [M][K]
+  int N, K;
+  int item0, S, sps;        // first item; row splits; 16-row sub-tiles per split
+  int part0, cnt0;          // first partial slot and counter (S > 1)
+};
+struct DecBwdBatch {
+  DecBwdProblem p[kDecMaxProblems];
+  int count, items, M, r;
+  float scale;
+  float* part;              // [slots][64][M rounded up to 4] fp32 partial sums
+  unsigned* cnt;            // arrival counters, one per split block column
+};
+DecChunkPlan dec_bwd_plan_chunk(int64_t M, int cn, const int64_t* N, const int64_t* K);
+size_t dec_bwd_workspace_bytes(int64_t M, int G, const int64_t* N, const int64_t* K);
+hipError_t launch_dec_bwd(int64_t M, int G, const uint16_t* const* dy, const int64_t* N, const int64_t* K,
+                          const uint8_t* const* packed, const int8_t* const* qscale, const float* const* step,
+                          const uint16_t* const* A, const uint16_t* const* B, int r, float alpha,
+                          uint16_t* const* dx, void* ws, const Codebook& cb, hipStream_t stream);
 
 // Tiled down-projection (M > kSmallM, and the adapter gradients): 64-row tiles
 // x KS splits of the contraction, `sps` 32-deep steps each; with KS > 1 the
@@ -125,37 +145,27 @@ inline DownPlan down_plan(int64_t M, int64_t Kc, int r) {
 }
 
 struct WsLayout {
-  size_t lora_off = 0, lora_bytes = 0;    // t or u (bf16 [M][rp], or fp32 partials)
-  size_t part_off = 0, part_bytes = 0;    // small-M backward partials
+  size_t lora_off = 0, lora_bytes = 0;    // t or u, bf16 [M][rp]
   size_t bt_off = 0, bt_bytes = 0;        // large-M backward: B transposed, bf16 [r][N]
   size_t dp_off = 0, dp_bytes = 0;        // large M: split partials of the down-projection
   size_t total = 0;
 };
 
 // op 0: forward (lora contraction over K); op 1: backward (over N). The
-// decode-shaped forward has its own layout (counters, then split partials).
+// decode-shaped kernels have their own layout (counters, then split partials).
 inline WsLayout ws_layout(int op, int64_t M, int64_t N, int64_t K, int r) {
   WsLayout w;
-  if (op == 0 && M <= kSmallM) {
-    w.total = dec_workspace_bytes(M, 1, &N, &K);
+  if (M <= kSmallM) {
+    w.total = op == 0 ? dec_workspace_bytes(M, 1, &N, &K) : dec_bwd_workspace_bytes(M, 1, &N, &K);
     return w;
   }
-  if (r > 0) {
-    const int64_t rp = rank_pad(r);
-    if (M > kSmallM)
-      w.lora_bytes = align256(static_cast<size_t>(M * rp * 2));
-    else                                       // u partials, one per row slice of the small-M backward
-      w.lora_bytes = align256(static_cast<size_t>(bwd_small_splits(N, K) * M * rp * 4));
-  }
+  if (r > 0) w.lora_bytes = align256(static_cast<size_t>(M * rank_pad(r) * 2));
   w.lora_off = kWsCounterBytes;
-  w.part_off = w.lora_off + w.lora_bytes;
-  if (op == 1 && M <= kSmallM)
-    w.part_bytes = align256(static_cast<size_t>(bwd_small_splits(N, K) * M * K * 4));
-  w.bt_off = w.part_off + w.part_bytes;
+  w.bt_off = w.lora_off + w.lora_bytes;
   if (op == 1 && M > kSmallM && r > 0) w.bt_bytes = align256(static_cast<size_t>(r) * N * 2);
   w.dp_off = w.bt_off + w.bt_bytes;
   if (M > kSmallM && r > 0) w.dp_bytes = down_plan(M, op == 0 ? K : N, r).part_bytes;
-  const size_t used = w.lora_bytes + w.part_bytes + w.bt_bytes + w.dp_bytes;
+  const size_t used = w.lora_bytes + w.bt_bytes + w.dp_bytes;
   w.total = used ? kWsCounterBytes + used : 0;
   return w;
 }
@@ -186,10 +196,6 @@ hipError_t launch_dequant(const uint8_t* packed, const int8_t* qscale, const flo
 // bf16); part: down_plan(M, Kc, r).part_bytes of workspace (bf16 path).
 hipError_t launch_lora_down(bool wrow, const uint16_t* in, int64_t M, int64_t Kc, const uint16_t* W, int r,
                             void* out, hipStream_t stream, uint16_t* wt, float* part, int64_t ldt = 0);
-hipError_t launch_bwd_small(const uint16_t* dy, int64_t M, int64_t N, int64_t K, const uint8_t* packed,
-                            const int8_t* qscale, const float* step, float* upart, int rp, const uint16_t* A,
-                            const uint16_t* B, int r, float scale, float* part, uint16_t* dx, const Codebook& cb,
-                            hipStream_t stream);
 
 // The forward of G weights, each with its own input x[i] (x[i] may repeat:
 // weights that share their input). Decode shapes run launch_dec_fwd over the
@@ -209,6 +215,15 @@ hipError_t launch_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K, co
                          const int8_t* qscale, const float* step, const uint16_t* A, const uint16_t* B,
                          int r, float alpha, uint16_t* dx, void* ws, const Codebook& cb,
                          hipStream_t stream);
+// The backward dX of G independent weights: decode shapes run launch_dec_bwd
+// over the whole table; larger M runs launch_bwd_dx per weight on one
+// workspace (bwd_batched_ws_bytes of it).
+hipError_t launch_bwd_dx_batched(int64_t M, int G, const uint16_t* const* dy, const int64_t* N, const int64_t* K,
+                                 const uint8_t* const* packed, const int8_t* const* qscale,
+                                 const float* const* step, const uint16_t* const* A, const uint16_t* const* B,
+                                 int r, float alpha, uint16_t* const* dx, void* ws, const Codebook& cb,
+                                 hipStream_t stream);
+size_t bwd_batched_ws_bytes(int64_t M, int G, const int64_t* N, const int64_t* K, int r);
 hipError_t launch_merge(const uint8_t* packed, const int8_t* qscale, const float* step, int64_t N, int64_t K,
                         const uint16_t* A, const uint16_t* B, int r, float alpha, uint16_t* out, const Codebook& cb,
                         hipStream_t stream);

@@ -42,11 +42,6 @@ __device__ __forceinline__ s16x4 ds_read_tr(const u32x4* base, int elem_off) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Workgroup barrier without the fence of __syncthreads (whose release half
-// waits for every outstanding vector load). The asm memory clobber keeps the
-// compiler from moving memory accesses across it; the caller waits for the
-// LDS DMA it needs published, and its own LDS reads of the buffer about to be
-// refilled have all been consumed by then.
 // Workgroup barrier without a fence: the wait for global loads in flight that
 // __syncthreads' fence implies is left out (prefetches stay in flight across
 // it); the caller waits for its own LDS writes and buffer-to-LDS loads first.

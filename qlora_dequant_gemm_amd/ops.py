@@ -351,6 +351,49 @@ def bwd_dx(dy, qw, A=None, B=None, alpha=0.0, out=None, ws=None):
     return out
 
 
+def bwd_dx_batched(dys, qws, As=None, Bs=None, alpha=0.0, outs=None, ws=None):
+    """The backward dX of independent linears, each with its own dY_i [M, N_i]:
+    [dY_i . deq(W_i) + (alpha/r) . (dY_i . B_i) . A_i for each i]. Decode
+    shapes stream all weights in one launch per 32 of them."""
+    G = len(qws)
+    if len(dys) != G:
+        raise ValueError("one dy per weight")
+    if (As is None) != (Bs is None) or (As is not None and (len(As) != G or len(Bs) != G)):
+        raise ValueError("As and Bs must both be None or both hold one adapter per weight")
+    if outs is not None and len(outs) != G:
+        raise ValueError("one output per weight")
+    M = _rows(dys[0], "dys[0]")
+    ranks = set()
+    for i, (dy, qw) in enumerate(zip(dys, qws)):
+        N, K = qw.shape
+        _shape(dy, (M, N), f"dys[{i}]")
+        ranks.add(_adapter_rank(As[i] if As is not None else None, Bs[i] if Bs is not None else None, N, K))
+        if outs is not None:
+            _shape(outs[i], (M, K), f"outs[{i}]")
+    if len(ranks) != 1:
+        raise ValueError("every weight must have adapters of one rank")
+    r = ranks.pop()
+    dev = dys[0].device
+    for i, (dy, qw) in enumerate(zip(dys, qws)):
+        _need(dy, torch.bfloat16, f"dys[{i}]", dev)
+        _check_weight(qw, dev)
+        _check_adapters(As[i] if As is not None else None, Bs[i] if Bs is not None else None, qw.shape[0],
+                        qw.shape[1], dev)
+    if outs is None:
+        outs = [torch.empty((M, qw.shape[1]), dtype=torch.bfloat16, device=dev) for qw in qws]
+    outs = [_check_out(o, (M, qw.shape[1]), dev, f"outs[{i}]") for i, (o, qw) in enumerate(zip(outs, qws))]
+    arr = lambda ts: (ctypes.c_void_p * G)(*[t.data_ptr() if t is not None else 0 for t in ts])
+    Ns = (ctypes.c_int64 * G)(*[qw.shape[0] for qw in qws])
+    Ks = (ctypes.c_int64 * G)(*[qw.shape[1] for qw in qws])
+    need = int(_lib.lib().qlora_workspace_bytes_bwd_batched(G, M, Ns, Ks, r))
+    wsb = (ws or Workspace(dev)).get(need)
+    _lib.check("qlora_nf4_bwd_dx_batched", _lib.lib().qlora_nf4_bwd_dx_batched(
+        G, M, arr(dys), Ns, Ks, arr([q.packed for q in qws]), arr([q.qscale for q in qws]),
+        arr([q.step for q in qws]), arr(As) if r else None, arr(Bs) if r else None, r, float(alpha), arr(outs),
+        _ptr(wsb), 0 if wsb is None else wsb.numel(), _stream(dev)))
+    return outs
+
+
 def lora_grad(x, dy, A, B, alpha, dA=None, dB=None, accumulate=False, ws=None):
     """Adapter gradients (dA [r, K], dB [N, r], fp32) of one QLoRA linear:
     dB = (alpha/r) . dY^T . bf16(x . A^T), dA = (alpha/r) . bf16(dY . B)^T . x.

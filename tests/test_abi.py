@@ -95,7 +95,11 @@ def test_workspace_sizes():
     assert ws(0, 16, 4096, 4096, 16) == C + 16 * 8 * 16 * 256 * 4
     assert ws(0, 1, 4096, 4096, 16) == C + 16 * 8 * 1 * 256 * 4
     assert ws(0, 16, 8, 64, 8) == 0
-    assert ws(1, 16, 4096, 4096, 0) > 0                           # small-M backward partials
+    # decode-shaped backward: 64 block columns x 8 splits of the rows (512
+    # rows each), fp32 partials [64][M rounded up to 4]
+    assert ws(1, 16, 4096, 4096, 0) == C + 64 * 8 * 64 * 16 * 4
+    assert ws(1, 1, 4096, 4096, 16) == C + 64 * 8 * 64 * 4 * 4
+    assert ws(1, 16, 512, 4096, 16) == 0                          # one split: no partials
     assert ws(1, 4096, 4096, 11008, 0) == 0
     assert ws(2, 16, 16, 64, 0) == 0 and ws(0, 0, 16, 64, 0) == 0
     for op in (0, 1, 2):
@@ -120,6 +124,18 @@ def test_workspace_sizes():
     K12 = (ctypes.c_int64 * 12)(*([4096] * 12))
     assert _lib.lib().qlora_workspace_bytes_batched(12, 4096, N12, K12, 16) == 8 * ws(0, 4096, 4096, 4096, 16)
     assert _lib.lib().qlora_workspace_bytes_batched(0, 16, N, K, 16) == 0
+    # the batched backward: one launch per 32 weights at decode shapes (one
+    # region of split partials), one call after another on larger M
+    assert _lib.lib().qlora_workspace_bytes_bwd_batched(3, 4096, N, K, 16) == max(ws(1, 4096, n, k, 16)
+                                                                                  for n, k in zip(N, K))
+    b = _lib.lib().qlora_workspace_bytes_bwd_batched(3, 16, N, K, 16)
+    assert b == 0 or (b >= C and (b - C) % (64 * 16 * 4) == 0)
+    N1 = (ctypes.c_int64 * 1)(4096)
+    K1 = (ctypes.c_int64 * 1)(4096)
+    assert _lib.lib().qlora_workspace_bytes_bwd_batched(1, 16, N1, K1, 16) == ws(1, 16, 4096, 4096, 16)
+    N1b = (ctypes.c_int64 * 1)(12)
+    assert _lib.lib().qlora_workspace_bytes_bwd_batched(1, 16, N1b, K1, 16) == 0      # N not a multiple of 8
+    assert _lib.lib().qlora_workspace_bytes_bwd_batched(0, 16, N, K, 16) == 0
 
 
 V = ctypes.c_void_p
@@ -184,7 +200,9 @@ def test_noalloc_forward_rejects_before_any_launch(kwargs, status):
 @pytest.mark.parametrize("kwargs,status", [
     (dict(dy=V(0)), 1), (dict(dx=V(0)), 1), (dict(N=12), 2), (dict(N=0), 2), (dict(K=100), 2),
     (dict(dy=ODD), 3), (dict(dx=ODD), 3), (dict(r=4, A=FAKE), 1),
-    (dict(ws=V(0), wsb=0), 5),
+    # 4096 rows at M = 16: the decode-shaped backward splits the rows, so a
+    # workspace is needed
+    (dict(N=4096, ws=V(0), wsb=0), 5),
 ])
 def test_backward_rejects_bad_arguments(kwargs, status):
     assert _bwd(**kwargs) == status
@@ -268,6 +286,26 @@ def test_thresholds_sit_well_inside_quantize_cells():
     frac = pos - np.floor(pos)
     assert np.min(np.minimum(frac, 1 - frac)) / 64 > 1e-4
     assert len(set(np.floor(pos).astype(int))) == 15
+
+
+def _bwd_batched(G=2, M=16, N=(64, 64), K=(64, 64), dy=FAKE, packed=FAKE, q=FAKE, step=FAKE, A=None, B=None,
+                 r=0, dx=FAKE, ws=V(0), wsb=0):
+    arr = lambda v: (ctypes.c_void_p * G)(*([v] * G)) if v is not None else None
+    Ns = (ctypes.c_int64 * G)(*N)
+    Ks = (ctypes.c_int64 * G)(*K)
+    return _lib.lib().qlora_nf4_bwd_dx_batched(G, M, arr(dy), Ns, Ks, arr(packed), arr(q), arr(step), arr(A),
+                                               arr(B), r, 1.0, arr(dx), ws, wsb, V(0))
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dy=V(0)), 1), (dict(dx=V(0)), 1), (dict(packed=V(0)), 1),
+    (dict(N=(64, 12)), 2), (dict(K=(64, 100)), 2), (dict(M=0), 2), (dict(G=0, N=(), K=()), 2),
+    (dict(dy=ODD), 3), (dict(dx=ODD), 3),
+    (dict(r=4), 1), (dict(r=4, A=FAKE), 1), (dict(r=129, A=FAKE, B=FAKE), 4),
+    (dict(N=(4096, 64), ws=V(0), wsb=0), 5),      # the decode shape splits the 4096 rows
+])
+def test_batched_backward_rejects_bad_arguments(kwargs, status):
+    assert _bwd_batched(**kwargs) == status
 
 
 def test_size_limits_return_shape_errors():

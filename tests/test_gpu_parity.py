@@ -233,6 +233,9 @@ BWD_CASES = [
     (300, 520, 320, 8, 16.0, 26),
     (513, 136, 576, 64, 16.0, 27),
     (260, 64, 64, 0, 0.0, 28),
+    (5, 136, 320, 5, 7.0, 29),         # odd rank: element loads of B rows
+    (3, 2000, 1024, 40, 16.0, 30),     # four rank tiles of 16; the rows split across workgroups
+    (16, 4096, 64, 16, 32.0, 31),      # one block column, the rows split across workgroups
 ]
 
 
@@ -877,6 +880,61 @@ def test_batched_forward_vs_oracle(qops, M, r, G, seed):
         assert _oracle_bound_ok(got, ref, S, T, alpha / max(r, 1)) == 0, (i, N, K)
 
 
+# ---------------------------------------------------------------------------
+# batched backward: independent dY and shapes per weight in one call
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,r,G,seed", [(1, 16, 5, 0), (16, 16, 7, 1), (4, 0, 3, 2), (3, 5, 4, 3),
+                                        (16, 64, 3, 4), (2, 32, 40, 6), (40, 16, 3, 7)])
+def test_batched_backward_vs_oracle(qops, M, r, G, seed):
+    """Weights of mixed shapes (K = 64 .. 11008, N a multiple of 8 up to
+    11008), each with its own dY: every output against the oracle
+    element-wise. G = 40 spans two launches (32 weights per launch); M = 40
+    takes the tiled path (one call per weight)."""
+    rng = np.random.Generator(np.random.PCG64(3700 + seed))
+    shapes = [(int(rng.choice([8, 64, 136, 520, 1000, 4096])), int(rng.choice([64, 320, 1024, 4096, 11008])))
+              for _ in range(G)]
+    if G >= 3:
+        shapes[0], shapes[1] = (4096, 4096), (11008, 1024)
+    if G > 8:
+        shapes = [(n, min(k, 1024)) for n, k in shapes]
+    alpha = 16.0
+    dys, ws, As, Bs = [], [], [], []
+    for i, (N, K) in enumerate(shapes):
+        dys.append(synth.activations(M, N, 3800 + 10 * seed + i))
+        ws.append(synth.weight(N, K, 3900 + 10 * seed + i))
+        A, B = synth.adapters(N, K, max(r, 1), 4000 + i, 4100 + i)
+        As.append(A)
+        Bs.append(B)
+    outs = qops.bwd_dx_batched([dev(d) for d in dys], [gpu_quant(qops, w) for w in ws],
+                               [dev(a) for a in As] if r else None, [dev(b) for b in Bs] if r else None, alpha)
+    for i, (N, K) in enumerate(shapes):
+        wd = _oracle_weight(ws[i])
+        ref = gemm.backward_dx(dys[i], wd, As[i], Bs[i], alpha, r)
+        got = to_f64(host_bits(outs[i]))
+        df = to_f64(dys[i])
+        S = np.abs(df) @ np.abs(to_f64(wd))
+        T = (np.abs(df @ to_f64(Bs[i])) @ np.abs(to_f64(As[i]))) if r else np.zeros_like(S)
+        assert _oracle_bound_ok(got, ref, S, T, alpha / max(r, 1)) == 0, (i, N, K)
+
+
+def test_batched_backward_repeats_bitwise(qops):
+    """Repeated identical batched calls through one workspace are bitwise
+    identical and leave its arrival counters zero."""
+    M, r = 16, 16
+    shapes = [(4096, 1024), (11008, 64), (520, 320)]
+    dys = [dev(synth.activations(M, N, 4200 + i)) for i, (N, K) in enumerate(shapes)]
+    qws = [gpu_quant(qops, synth.weight(N, K, 4300 + i)) for i, (N, K) in enumerate(shapes)]
+    ad = [synth.adapters(N, K, r, 4400 + i, 4500 + i) for i, (N, K) in enumerate(shapes)]
+    As, Bs = [dev(a) for a, _ in ad], [dev(b) for _, b in ad]
+    ws = qops.Workspace("cuda")
+    o1 = qops.bwd_dx_batched(dys, qws, As, Bs, 32.0, ws=ws)
+    torch.cuda.synchronize()
+    assert int(ws.buf[:16384].view(torch.int32).abs().sum()) == 0
+    o2 = qops.bwd_dx_batched(dys, qws, As, Bs, 32.0, ws=ws)
+    for a, b in zip(o1, o2):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 def test_decode_split_fixup_counters_left_zero(qops):
     """A call whose K is split across workgroups leaves the workspace's arrival
     counters zero, so the same workspace serves any later call; repeated calls
@@ -892,3 +950,20 @@ def test_decode_split_fixup_counters_left_zero(qops):
     assert int(ws.buf[:16384].view(torch.int32).abs().sum()) == 0
     y2 = qops.lora_fwd(x, qw, A, B, 32.0, ws=ws)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_decode_bwd_split_fixup_counters_left_zero(qops):
+    """A decode-shaped backward whose rows are split across workgroups leaves
+    the workspace's arrival counters zero; repeated calls through one
+    workspace are bitwise identical."""
+    M, N, K, r = 16, 11008, 1024, 16
+    dy = dev(synth.activations(M, N, 3600))
+    qw = gpu_quant(qops, synth.weight(N, K, 3601))
+    A, B = (dev(a) for a in synth.adapters(N, K, r, 3602, 3603))
+    ws = qops.Workspace("cuda")
+    assert qops.workspace_bytes(1, M, N, K, r) > 16384
+    d1 = qops.bwd_dx(dy, qw, A, B, 32.0, ws=ws)
+    torch.cuda.synchronize()
+    assert int(ws.buf[:16384].view(torch.int32).abs().sum()) == 0
+    d2 = qops.bwd_dx(dy, qw, A, B, 32.0, ws=ws)
+    assert torch.equal(d1.view(torch.int16), d2.view(torch.int16))
