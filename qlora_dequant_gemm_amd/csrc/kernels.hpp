@@ -75,6 +75,7 @@ struct DecFwdBatch {
 struct DecChunkPlan {
   int S[kDecMaxProblems], sps[kDecMaxProblems];
   int64_t slots = 0, counters = 0, items = 0;
+  bool wide = false;        // decode-shaped backward: the item shape
 };
 DecChunkPlan dec_plan_chunk(int64_t M, int cn, const int64_t* N, const int64_t* K);
 size_t dec_workspace_bytes(int64_t M, int G, const int64_t* N, const int64_t* K);
@@ -85,10 +86,16 @@ hipError_t launch_dec_fwd(int64_t M, int G, const uint16_t* const* x, const int6
                           uint16_t* const* y, void* ws, const Codebook& cb, hipStream_t stream);
 
 // Decode-shaped backward (M <= kSmallM) over a table of weights, one launch
-// per chunk of kDecMaxProblems: items are 64-column block columns of dX x S_p
-// ranges of the weight's rows (64-row sub-tiles, at least kDbMinSps per range).
+// per chunk of kDecMaxProblems. A launch whose weights have fewer than
+// kDbWideMin 256-column ranges in all runs narrow items (64 columns x S_p
+// ranges of the weight's rows, at least kDbMinSps 64-row sub-tiles each,
+// about kDbTargetItems items); larger launches run wide items (256 columns x
+// at most kDwMaxSps super-steps of 256 rows, about kDbWideTarget items).
+constexpr int64_t kDbWideMin = 128;
 constexpr int64_t kDbMinSps = 8;
 constexpr int64_t kDbTargetItems = 1024;
+constexpr int kDwMaxSps = 4;
+constexpr int64_t kDbWideTarget = 512;
 struct DecBwdProblem {
   const uint16_t* dy;       // [M][N]
   const uint8_t* packed;    // stored weight [N][K]
@@ -98,15 +105,15 @@ struct DecBwdProblem {
   const uint16_t* B;        // [N][r]
   uint16_t* dx;             // [M][K]
   int N, K;
-  int item0, S, sps;        // first item; row splits; 16-row sub-tiles per split
+  int item0, S, sps;        // first item; row splits; sub-tiles (narrow) or super-steps (wide) per split
   int part0, cnt0;          // first partial slot and counter (S > 1)
 };
 struct DecBwdBatch {
   DecBwdProblem p[kDecMaxProblems];
   int count, items, M, r;
   float scale;
-  float* part;              // [slots][64][M rounded up to 4] fp32 partial sums
-  unsigned* cnt;            // arrival counters, one per split block column
+  float* part;              // [slots][64 or 256 columns][M rounded up to 4] fp32 partial sums
+  unsigned* cnt;            // arrival counters, one per split column range
 };
 DecChunkPlan dec_bwd_plan_chunk(int64_t M, int cn, const int64_t* N, const int64_t* K);
 size_t dec_bwd_workspace_bytes(int64_t M, int G, const int64_t* N, const int64_t* K);

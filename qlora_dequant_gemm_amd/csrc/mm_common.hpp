@@ -54,6 +54,10 @@ template <typename A, typename B, typename C, typename D>
 __device__ __forceinline__ void lds_barrier_on(A* a, B* b, C* c, D* d) {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::"s"(a), "s"(b), "s"(c), "s"(d) : "memory");
 }
+template <typename A, typename B, typename C, typename D, typename E, typename F>
+__device__ __forceinline__ void lds_barrier_on(A* a, B* b, C* c, D* d, E* e, F* f) {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::"s"(a), "s"(b), "s"(c), "s"(d), "s"(e), "s"(f) : "memory");
+}
 
 // s_waitcnt vmcnt(n) with expcnt/lgkmcnt left alone (gfx9 encoding: vmcnt
 // bits 3:0 and 15:14), as the builtin so that the compiler's own wait

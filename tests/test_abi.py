@@ -95,8 +95,8 @@ def test_workspace_sizes():
     assert ws(0, 16, 4096, 4096, 16) == C + 16 * 8 * 16 * 256 * 4
     assert ws(0, 1, 4096, 4096, 16) == C + 16 * 8 * 1 * 256 * 4
     assert ws(0, 16, 8, 64, 8) == 0
-    # decode-shaped backward: 64 block columns x 8 splits of the rows (512
-    # rows each), fp32 partials [64][M rounded up to 4]
+    # decode-shaped backward, one weight: 64 block columns x 8 splits of the
+    # rows (512 rows each), fp32 partials [64][M rounded up to 4]
     assert ws(1, 16, 4096, 4096, 0) == C + 64 * 8 * 64 * 16 * 4
     assert ws(1, 1, 4096, 4096, 16) == C + 64 * 8 * 64 * 4 * 4
     assert ws(1, 16, 512, 4096, 16) == 0                          # one split: no partials
@@ -133,6 +133,10 @@ def test_workspace_sizes():
     N1 = (ctypes.c_int64 * 1)(4096)
     K1 = (ctypes.c_int64 * 1)(4096)
     assert _lib.lib().qlora_workspace_bytes_bwd_batched(1, 16, N1, K1, 16) == ws(1, 16, 4096, 4096, 16)
+    # eight 4096 x 4096 weights take 256-column items: 16 column ranges x 4
+    # splits (1024 rows each) per weight, partials [256][16]
+    N8 = (ctypes.c_int64 * 8)(*([4096] * 8))
+    assert _lib.lib().qlora_workspace_bytes_bwd_batched(8, 16, N8, N8, 16) == C + 8 * 16 * 4 * 256 * 16 * 4
     N1b = (ctypes.c_int64 * 1)(12)
     assert _lib.lib().qlora_workspace_bytes_bwd_batched(1, 16, N1b, K1, 16) == 0      # N not a multiple of 8
     assert _lib.lib().qlora_workspace_bytes_bwd_batched(0, 16, N, K, 16) == 0

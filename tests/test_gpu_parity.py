@@ -917,6 +917,32 @@ def test_batched_backward_vs_oracle(qops, M, r, G, seed):
         assert _oracle_bound_ok(got, ref, S, T, alpha / max(r, 1)) == 0, (i, N, K)
 
 
+@pytest.mark.parametrize("M,r,K,seed", [(16, 16, 4096, 0), (3, 5, 4032, 1), (1, 32, 4096, 2), (8, 0, 4032, 3)])
+def test_batched_backward_wide_items_vs_oracle(qops, M, r, K, seed):
+    """Eight weights sharing K (128 or more 256-column ranges in the launch,
+    so the backward runs its 256-column items; K = 4032 leaves a ragged last
+    range): every output against the oracle element-wise."""
+    Ns = [4096, 2000, 520, 8, 11008, 4096, 1000, 64]
+    alpha = 16.0
+    dys, ws, As, Bs = [], [], [], []
+    for i, N in enumerate(Ns):
+        dys.append(synth.activations(M, N, 4600 + 10 * seed + i))
+        ws.append(synth.weight(N, K, 4700 + 10 * seed + i))
+        A, B = synth.adapters(N, K, max(r, 1), 4800 + i, 4900 + i)
+        As.append(A)
+        Bs.append(B)
+    outs = qops.bwd_dx_batched([dev(d) for d in dys], [gpu_quant(qops, w) for w in ws],
+                               [dev(a) for a in As] if r else None, [dev(b) for b in Bs] if r else None, alpha)
+    for i, N in enumerate(Ns):
+        wd = _oracle_weight(ws[i])
+        ref = gemm.backward_dx(dys[i], wd, As[i], Bs[i], alpha, r)
+        got = to_f64(host_bits(outs[i]))
+        df = to_f64(dys[i])
+        S = np.abs(df) @ np.abs(to_f64(wd))
+        T = (np.abs(df @ to_f64(Bs[i])) @ np.abs(to_f64(As[i]))) if r else np.zeros_like(S)
+        assert _oracle_bound_ok(got, ref, S, T, alpha / max(r, 1)) == 0, (i, N, K)
+
+
 def test_batched_backward_repeats_bitwise(qops):
     """Repeated identical batched calls through one workspace are bitwise
     identical and leave its arrival counters zero."""
