@@ -228,45 +228,40 @@ class StackWorkload:
         self.M, self.r, self.alpha = synth.STACK_M, synth.STACK_R, synth.STACK_ALPHA
         self.Ms, self.bwd_M, self.decode, self.C = [self.M], [self.M], False, 1
         self.lay = []
-        qstream = torch.cuda.Stream()
-        qev = []
         for l in range(self.L):
             row = []
             for j in range(len(self.lin)):
                 d = synth.stack_linear_device(l, j, self.M)
-                w = d.pop("w")
-                N, K = w.shape
-                nb = N * K // 64
-                packed = torch.empty(N * K // 2, dtype=torch.uint8, device="cuda")
-                absmax = torch.empty(nb, dtype=torch.float32, device="cuda")
-                q = torch.empty(nb, dtype=torch.int8, device="cuda")
-                st = torch.empty((nb + 255) // 256, dtype=torch.float32, device="cuda")
-                torch.cuda.synchronize()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                with torch.cuda.stream(qstream):
-                    # keep the stream busy while the host issues the launch, so
-                    # that the events bracket the kernel and not the host's
-                    # argument checks and launch latency
-                    if hasattr(torch.cuda, "_sleep"):
-                        torch.cuda._sleep(2_000_000)
-                    e0.record(qstream)
-                    ops.quantize_dq(w, packed=packed, absmax=absmax, q=q, step=st)
-                    e1.record(qstream)
-                d["qw"] = ops.NF4Weight(packed, q, st, (N, K))
-                qev.append((e0, e1, w.numel()))
-                torch.cuda.synchronize()
-                del w
+                d["qw"] = ops.quantize_weight(d.pop("w"))
                 row.append(d)
             self.lay.append(row)
         torch.cuda.synchronize()
-        qms = sum(e0.elapsed_time(e1) for e0, e1, _ in qev)
-        qbytes = sum(quantize_bytes(n, 1) for _, _, n in qev)
-        self.quantize = {"ms_total": round(qms, 4), "weights": len(qev), "GB/s": round(qbytes / qms / 1e6, 1),
+        # quantize + double quant, timed as the seven quantize launches of one
+        # layer captured in one graph (layer 0's fp32 weights drawn again from
+        # their seeds: 0.77 GB together, beyond the last-level cache), times
+        # the layer count
+        qin = []
+        for j in range(len(self.lin)):
+            w = synth.stack_linear_device(0, j, self.M, acts=None)["w"]
+            N, K = w.shape
+            nb = N * K // 64
+            qin.append((w, torch.empty(N * K // 2, dtype=torch.uint8, device="cuda"),
+                        torch.empty(nb, dtype=torch.float32, device="cuda"),
+                        torch.empty(nb, dtype=torch.int8, device="cuda"),
+                        torch.empty((nb + 255) // 256, dtype=torch.float32, device="cuda")))
+        qstream = torch.cuda.Stream()
+        g = graph_of([lambda a=a: ops.quantize_dq(a[0], packed=a[1], absmax=a[2], q=a[3], step=a[4]) for a in qin],
+                     qstream)
+        qms = time_graph(g, qstream, 5) * self.L
+        qbytes = sum(quantize_bytes(a[0].numel(), 1) for a in qin) * self.L
+        del g, qin
+        self.quantize = {"ms_total": round(qms, 4), "weights": self.L * len(self.lin),
+                         "GB/s": round(qbytes / qms / 1e6, 1),
                          "hbm_frac": round(qbytes / qms / 1e6 / HBM_PEAK_GBS, 4), "algorithmic_bytes": qbytes,
                          "kernel": "k_quantize",
-                         "note": "fp32 W read once + NF4 codes, absmax, int8 scales and steps written once, "
-                                 "summed over the 224 quantize launches as the stack is loaded (each weight "
-                                 "freshly drawn, 64-180 MB of fp32)"}
+                         "note": "fp32 W read once + NF4 codes, absmax, int8 scales and steps written once; "
+                                 "the seven quantize launches of one layer (64-180 MB of fp32 each) timed as one "
+                                 "graph, times the layer count"}
         self.nf4_bytes = sum(d["qw"].nbytes for row in self.lay for d in row)
         self.y = {N: torch.empty((self.M, N), dtype=torch.bfloat16, device="cuda") for _, N, _ in self.lin}
         self.dx = {K: torch.empty((self.M, K), dtype=torch.bfloat16, device="cuda") for _, _, K in self.lin}
