@@ -605,7 +605,7 @@ def _merge_mag(wd, A, B, alpha, r):
 
 
 @pytest.mark.parametrize("N,K,r,alpha,seed", [(300, 320, 16, 32.0, 0), (37, 64, 5, 7.0, 1), (130, 1024, 64, 16.0, 2),
-                                              (8, 576, 128, 8.0, 3)])
+                                              (8, 576, 128, 8.0, 3), (200, 512, 40, 16.0, 4), (64, 256, 100, 8.0, 5)])
 def test_merge_parity(qops, N, K, r, alpha, seed):
     w = synth.weight(N, K, 800 + seed)
     A, B = synth.adapters(N, K, r, 810 + seed, 820 + seed)
