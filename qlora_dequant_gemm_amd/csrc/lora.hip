@@ -115,13 +115,13 @@ constexpr int kDownWaves = 8;
 
 template <int RT, int GS>
 __global__ __launch_bounds__(64 * kDownWaves) void k_down_rows(const uint16_t* in, int M, int Kc, const uint16_t* W, int r,
-                                                   int rp, uint16_t* __restrict__ out) {
+                                                   int rp, uint16_t* __restrict__ out, int ldt) {
   __shared__ f32x4 red[kDownWaves][RT][64];
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int g = lane >> 4, c = lane & 15;
   const int m0 = blockIdx.x * 16;
-  const int rows_valid = M - m0 < 16 ? M - m0 : 16;
+  const int rows_valid = M - m0 < 0 ? 0 : (M - m0 < 16 ? M - m0 : 16);
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(in + static_cast<int64_t>(m0) * Kc), 0, rows_valid * Kc * 2, kBufWord3);
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(W), 0, r * Kc * 2,
@@ -167,10 +167,11 @@ __global__ __launch_bounds__(64 * kDownWaves) void k_down_rows(const uint16_t* i
 #pragma unroll
   for (int jt = 0; jt < RT; ++jt) red[w][jt][lane] = acc[jt];
   __syncthreads();
-  // lane (g, c) of a fragment holds rows 4 g + v, rank 16 jt + c
+  // lane (g, c) of a fragment holds rows 4 g + v, rank 16 jt + c; ldt > 0:
+  // written transposed, [rp][ldt], with the rows past M (zero sums) as well
   for (int e = t; e < 16 * rp; e += 64 * kDownWaves) {
-    const int row = e / rp, j = e - (e / rp) * rp;
-    if (row >= rows_valid) continue;
+    const int row = ldt ? e & 15 : e / rp, j = ldt ? e >> 4 : e - (e / rp) * rp;
+    if (ldt ? m0 + row >= ldt : row >= rows_valid) continue;
     float sum = 0.f;
     if (j < 16 * RT) {
       const int jt = j >> 4, l = ((row >> 2) << 4) | (j & 15);
@@ -178,7 +179,10 @@ __global__ __launch_bounds__(64 * kDownWaves) void k_down_rows(const uint16_t* i
 #pragma unroll
       for (int ww = 0; ww < kDownWaves; ++ww) sum += red[ww][jt][l][v];
     }
-    out[static_cast<int64_t>(m0 + row) * rp + j] = bf16_bits(sum);
+    if (ldt)
+      out[static_cast<int64_t>(j) * ldt + m0 + row] = bf16_bits(sum);
+    else
+      out[static_cast<int64_t>(m0 + row) * rp + j] = bf16_bits(sum);
   }
 }
 
@@ -225,24 +229,24 @@ hipError_t launch_lora_down(bool wrow, const uint16_t* in, int64_t M, int64_t Kc
     hipLaunchKernelGGL(k_adapter_t, dim3(static_cast<unsigned>(cdiv(Kc, 64))), dim3(256), 0, stream, W, Kc, r, wt);
     Wr = wt;
   }
-  if (!ldt && M > 16) {
-    // the matmul paths: row-streaming form, no split partials
-    const unsigned grid16 = static_cast<unsigned>(cdiv(M, 16));
-    const int mi = static_cast<int>(M), kci = static_cast<int>(Kc);
+  if (M > 16) {
+    // row-streaming form, no split partials (ldt: the rows up to ldt too)
+    const unsigned grid16 = static_cast<unsigned>(cdiv(ldt ? ldt : M, 16));
+    const int mi = static_cast<int>(M), kci = static_cast<int>(Kc), lt = static_cast<int>(ldt);
     uint16_t* o16 = static_cast<uint16_t*>(out);
     const int nt = down_nt(r);
     if (nt == 1)
       hipLaunchKernelGGL(HIP_KERNEL_NAME(k_down_rows<1, 4>), dim3(grid16), dim3(64 * kDownWaves), 0, stream, in, mi, kci, Wr, r,
-                         rp, o16);
+                         rp, o16, lt);
     else if (nt == 2)
       hipLaunchKernelGGL(HIP_KERNEL_NAME(k_down_rows<2, 4>), dim3(grid16), dim3(64 * kDownWaves), 0, stream, in, mi, kci, Wr, r,
-                         rp, o16);
+                         rp, o16, lt);
     else if (nt == 4)
       hipLaunchKernelGGL(HIP_KERNEL_NAME(k_down_rows<4, 2>), dim3(grid16), dim3(64 * kDownWaves), 0, stream, in, mi, kci, Wr, r,
-                         rp, o16);
+                         rp, o16, lt);
     else
       hipLaunchKernelGGL(HIP_KERNEL_NAME(k_down_rows<8, 1>), dim3(grid16), dim3(64 * kDownWaves), 0, stream, in, mi, kci, Wr, r,
-                         rp, o16);
+                         rp, o16, lt);
     return hipGetLastError();
   }
   const DownPlan p = down_plan(M, Kc, r);
