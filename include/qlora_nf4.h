@@ -154,7 +154,12 @@ size_t qlora_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int r);
  *   workspace / ws_bytes  device scratch of at least
  *           qlora_workspace_bytes(0, M, N, K, r) bytes, 16-byte aligned
  *           (may be NULL when that is 0). Its contents are overwritten.
- * Products are bf16 x bf16 accumulated in fp32. x, packed, y, A, B and the
+ * Products are bf16 x bf16 accumulated in fp32. For M <= 16 the kernel
+ * streams the weight with the contraction over K split across workgroups
+ * when that fills the chip; each split then carries its part of
+ * (alpha / r) . t as the sum of two bf16 values (about 16 significant bits)
+ * rather than one rounding of the full t, a difference below one bf16
+ * rounding of the LoRA term. x, packed, y, A, B and the
  * workspace must be 16-byte aligned. Size limits (here and in every other
  * matmul call: grouped forward, backward, merge, adapter gradients):
  * M <= 2^31, N and K <= 2^21 (each operand is addressed through 32-bit
@@ -271,6 +276,9 @@ size_t qlora_workspace_bytes_batched(int G, int64_t M, const int64_t* N,
  *   A, B, r, alpha  as in the forward; NULL/0 gives the base term only.
  *   dx      [M, K] bf16 out.
  *   workspace / ws_bytes  at least qlora_workspace_bytes(1, M, N, K, r).
+ * For M <= 16 the contraction over N is split across workgroups when that
+ * fills the chip, and each split carries its part of (alpha / r) . u as the
+ * sum of two bf16 values (as the forward does with t at these shapes).
  */
 int qlora_nf4_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K,
                      const uint8_t* packed, const int8_t* qscale,

@@ -15,7 +15,7 @@
 //   k_gemm_bwd    M > 16: same tiling over dX [M, K]; the contraction runs over
 //                 W's rows, so the dequantized tile is stored row-major and
 //                 read transposed with ds_read_b64_tr_b16.
-// The rank-r down projections t and u come from k_down (lora.hip).
+// The rank-r down projections t and u come from k_down_rows (lora.hip).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
