@@ -110,18 +110,38 @@ __global__ __launch_bounds__(256) void k_down(const uint16_t* in, int64_t M, int
 // row 16 jt + c the same elements (a contraction is order-free). Kc % 8 == 0:
 // 8-element pieces past Kc are zeroed; rows past M and adapter rows past r
 // read as zero through the descriptors.
+// kBT: the adapter is B [Kc][r] with r = 16 RT, read in place rather than
+// through a transposed copy: each wave copies the B rows of its GS chunks
+// (64 rows x 32 RT bytes each, one contiguous run) into its own LDS region
+// and reads the operands back with ds_read_b64_tr_b16, whose 16-lane groups
+// return one rank column of 4 consecutive rows per lane. The 32-byte pieces
+// (row R, rank tile jt) sit at (R RT + jt) ^ bt_swz(R), which keeps both the
+// 16-byte copies and the transposed reads (two lane groups per 256-byte
+// phase) on 64 distinct banks.
 // ---------------------------------------------------------------------------
 constexpr int kDownWaves = 8;
 
-template <int RT, int GS>
+template <int RT>
+__device__ __forceinline__ int bt_swz(int R) {
+  if constexpr (RT == 1) return ((R >> 4) & 1) << 2;
+  else if constexpr (RT == 2) return (R >> 4) & 1;
+  else if constexpr (RT == 4) return ((R >> 1) & 1) | (((R >> 4) & 1) << 1);
+  else return (R & 3) | (((R >> 4) & 1) << 2);
+}
+
+template <int RT, int GS, bool kBT>
 __global__ __launch_bounds__(64 * kDownWaves) void k_down_rows(const uint16_t* in, int M, int Kc, const uint16_t* W, int r,
                                                    int rp, uint16_t* __restrict__ out, int ldt) {
-  __shared__ f32x4 red[kDownWaves][RT][64];
+  // per wave: the staged adapter rows of a round (kBT), then its partial sums
+  constexpr int kStage = kBT ? GS * 128 * RT : 0;          // 16-byte chunks
+  constexpr int kPer = kStage > 64 * RT ? kStage : 64 * RT;
+  __shared__ u32x4 lds[kDownWaves * kPer];
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int g = lane >> 4, c = lane & 15;
   const int m0 = blockIdx.x * 16;
   const int rows_valid = M - m0 < 0 ? 0 : (M - m0 < 16 ? M - m0 : 16);
+  u32x4* const mine = lds + w * kPer;
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(in + static_cast<int64_t>(m0) * Kc), 0, rows_valid * Kc * 2, kBufWord3);
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(W), 0, r * Kc * 2,
@@ -138,17 +158,48 @@ __global__ __launch_bounds__(64 * kDownWaves) void k_down_rows(const uint16_t* i
   // GS chunks per round, all their loads issued before their MFMAs
   for (int q0 = w; q0 < nchunk; q0 += kDownWaves * GS) {
     u32x4 xa[GS][2], wa[GS][RT][2];
+    u32x4 bl[kBT ? GS : 1][kBT ? 2 * RT : 1];
 #pragma unroll
     for (int u = 0; u < GS; ++u) {
       const int q = q0 + kDownWaves * u < nchunk ? q0 + kDownWaves * u : nchunk - 1;
       const uint32_t so = static_cast<uint32_t>(q * 128);
       xa[u][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xo, so, 0));
       xa[u][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xo + 16, so, 0));
+      if constexpr (kBT) {
+        // B rows 64 q .. 64 q + 63: 16-byte piece lane + 64 e of the run
+        const uint32_t bo = static_cast<uint32_t>(q * 2048 * RT);
 #pragma unroll
-      for (int jt = 0; jt < RT; ++jt) {
-        wa[u][jt][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, wo[jt], so, 0));
-        wa[u][jt][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, wo[jt] + 16, so, 0));
+        for (int e = 0; e < 2 * RT; ++e)
+          bl[u][e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, 16 * (lane + 64 * e), bo, 0));
+      } else {
+#pragma unroll
+        for (int jt = 0; jt < RT; ++jt) {
+          wa[u][jt][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, wo[jt], so, 0));
+          wa[u][jt][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, wo[jt] + 16, so, 0));
+        }
       }
+    }
+    if constexpr (kBT) {
+#pragma unroll
+      for (int u = 0; u < GS; ++u)
+#pragma unroll
+        for (int e = 0; e < 2 * RT; ++e) {
+          const int pc = lane + 64 * e, sl = pc >> 1, R = sl / RT;
+          mine[u * 128 * RT + 2 * (sl ^ bt_swz<RT>(R)) + (pc & 1)] = bl[u][e];
+        }
+#pragma unroll
+      for (int u = 0; u < GS; ++u)
+#pragma unroll
+        for (int jt = 0; jt < RT; ++jt) {
+          s16x4 v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int R = 16 * g + 4 * i + (c >> 2);
+            v[i] = ds_read_tr(mine + u * 128 * RT, 16 * ((R * RT + jt) ^ bt_swz<RT>(R)) + 4 * (c & 3));
+          }
+          wa[u][jt][0] = __builtin_bit_cast(u32x4, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+          wa[u][jt][1] = __builtin_bit_cast(u32x4, __builtin_shufflevector(v[2], v[3], 0, 1, 2, 3, 4, 5, 6, 7));
+        }
     }
 #pragma unroll
     for (int u = 0; u < GS; ++u) {
@@ -164,8 +215,11 @@ __global__ __launch_bounds__(64 * kDownWaves) void k_down_rows(const uint16_t* i
       }
     }
   }
+  // the wave's own region takes its partial sums (its last reads of the
+  // staged rows come before these writes in its LDS order)
+  f32x4* const red = reinterpret_cast<f32x4*>(lds);
 #pragma unroll
-  for (int jt = 0; jt < RT; ++jt) red[w][jt][lane] = acc[jt];
+  for (int jt = 0; jt < RT; ++jt) red[w * kPer + jt * 64 + lane] = acc[jt];
   __syncthreads();
   // lane (g, c) of a fragment holds rows 4 g + v, rank 16 jt + c; ldt > 0:
   // written transposed, [rp][ldt], with the rows past M (zero sums) as well
@@ -177,7 +231,7 @@ __global__ __launch_bounds__(64 * kDownWaves) void k_down_rows(const uint16_t* i
       const int jt = j >> 4, l = ((row >> 2) << 4) | (j & 15);
       const int v = row & 3;
 #pragma unroll
-      for (int ww = 0; ww < kDownWaves; ++ww) sum += red[ww][jt][l][v];
+      for (int ww = 0; ww < kDownWaves; ++ww) sum += red[ww * kPer + jt * 64 + l][v];
     }
     if (ldt)
       out[static_cast<int64_t>(j) * ldt + m0 + row] = bf16_bits(sum);
@@ -224,30 +278,43 @@ __global__ __launch_bounds__(256) void k_adapter_t(const uint16_t* __restrict__ 
 hipError_t launch_lora_down(bool wrow, const uint16_t* in, int64_t M, int64_t Kc, const uint16_t* W, int r,
                             void* out, hipStream_t stream, uint16_t* wt, float* part, int64_t ldt) {
   const int rp = static_cast<int>(rank_pad(r));
+  const int nt = down_nt(r);
+  if (M > 16) {
+    // row-streaming form, no split partials (ldt: the rows up to ldt too);
+    // B with r = 16 nt is read in place, other ranks through Bt
+    const bool in_place = !wrow && r == 16 * nt;
+    const uint16_t* Wr = W;
+    if (!wrow && !in_place) {
+      hipLaunchKernelGGL(k_adapter_t, dim3(static_cast<unsigned>(cdiv(Kc, 64))), dim3(256), 0, stream, W, Kc, r, wt);
+      Wr = wt;
+    }
+    const unsigned grid16 = static_cast<unsigned>(cdiv(ldt ? ldt : M, 16));
+    const int mi = static_cast<int>(M), kci = static_cast<int>(Kc), lt = static_cast<int>(ldt);
+    uint16_t* o16 = static_cast<uint16_t*>(out);
+#define QNF4_DR(RTV, GSV)                                                                                     \
+  do {                                                                                                        \
+    if (in_place)                                                                                             \
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(k_down_rows<RTV, GSV, true>), dim3(grid16), dim3(64 * kDownWaves), 0, \
+                         stream, in, mi, kci, Wr, r, rp, o16, lt);                                            \
+    else                                                                                                      \
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(k_down_rows<RTV, GSV, false>), dim3(grid16), dim3(64 * kDownWaves), 0, \
+                         stream, in, mi, kci, Wr, r, rp, o16, lt);                                            \
+  } while (0)
+    if (nt == 1)
+      QNF4_DR(1, 4);
+    else if (nt == 2)
+      QNF4_DR(2, 4);
+    else if (nt == 4)
+      QNF4_DR(4, 2);
+    else
+      QNF4_DR(8, 1);
+#undef QNF4_DR
+    return hipGetLastError();
+  }
   const uint16_t* Wr = W;
   if (!wrow) {
     hipLaunchKernelGGL(k_adapter_t, dim3(static_cast<unsigned>(cdiv(Kc, 64))), dim3(256), 0, stream, W, Kc, r, wt);
     Wr = wt;
-  }
-  if (M > 16) {
-    // row-streaming form, no split partials (ldt: the rows up to ldt too)
-    const unsigned grid16 = static_cast<unsigned>(cdiv(ldt ? ldt : M, 16));
-    const int mi = static_cast<int>(M), kci = static_cast<int>(Kc), lt = static_cast<int>(ldt);
-    uint16_t* o16 = static_cast<uint16_t*>(out);
-    const int nt = down_nt(r);
-    if (nt == 1)
-      hipLaunchKernelGGL(HIP_KERNEL_NAME(k_down_rows<1, 4>), dim3(grid16), dim3(64 * kDownWaves), 0, stream, in, mi, kci, Wr, r,
-                         rp, o16, lt);
-    else if (nt == 2)
-      hipLaunchKernelGGL(HIP_KERNEL_NAME(k_down_rows<2, 4>), dim3(grid16), dim3(64 * kDownWaves), 0, stream, in, mi, kci, Wr, r,
-                         rp, o16, lt);
-    else if (nt == 4)
-      hipLaunchKernelGGL(HIP_KERNEL_NAME(k_down_rows<4, 2>), dim3(grid16), dim3(64 * kDownWaves), 0, stream, in, mi, kci, Wr, r,
-                         rp, o16, lt);
-    else
-      hipLaunchKernelGGL(HIP_KERNEL_NAME(k_down_rows<8, 1>), dim3(grid16), dim3(64 * kDownWaves), 0, stream, in, mi, kci, Wr, r,
-                         rp, o16, lt);
-    return hipGetLastError();
   }
   const DownPlan p = down_plan(M, Kc, r);
   const unsigned grid = static_cast<unsigned>(cdiv(M, 64) * p.KS);

@@ -236,6 +236,8 @@ BWD_CASES = [
     (5, 136, 320, 5, 7.0, 29),         # odd rank: element loads of B rows
     (3, 2000, 1024, 40, 16.0, 30),     # four rank tiles of 16; the rows split across workgroups
     (16, 4096, 64, 16, 32.0, 31),      # one block column, the rows split across workgroups
+    (40, 200, 128, 32, 16.0, 32),      # B read in place, two rank tiles, a partial last chunk of N
+    (33, 72, 64, 128, 8.0, 33),        # B read in place, eight rank tiles
 ]
 
 
