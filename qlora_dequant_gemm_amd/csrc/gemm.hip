@@ -460,16 +460,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd(FwdTable tab, int64_t M, in
 // ---------------------------------------------------------------------------
 // k_gemm_bwd: dX [M, K] = dY . W' (+ LoRA), M > 16.
 //
-// Workgroup tile 256 (M) x 256 (K), four waves as 2 x 2, each 128 x 128:
-// 4 x 4 blocks of 32x32x16 bf16 MFMA. The contraction runs over W's rows (N)
-// in steps of 64, so the weights are needed transposed: each step the
-// workgroup decodes the 64 x 256 slice of W' (one 64-block per thread) into
-// LDS, row-major, and the waves read their B operands with ds_read_b64_tr_b16.
+// Workgroup tile 256 (M) x 256 (K), eight waves (two per SIMD) as 2 x 4, each
+// 128 x 64: 4 x 2 blocks of 32x32x16 bf16 MFMA. The contraction runs over W's
+// rows (N) in steps of 64, so the weights are needed transposed: each step
+// the workgroup decodes the 64 x 256 slice of W' (half a 64-block per thread,
+// every weight once) into LDS, row-major, and the waves read their B operands
+// with ds_read_b64_tr_b16. Two waves per SIMD let one wave's MFMAs issue
+// while the other waits on its LDS reads, its decode or the step barrier.
 // Per step k:
-//   dY    tile k+1 (256 x 64) requested by DMA into the other slot of a
-//         two-slot ring (buffer_load ... lds; rows past M read as zero);
-//   codes of step k+2 loaded into registers (128 contiguous bytes per weight
-//         row, four threads a row);
+//   dY    tile k+1 (256 x 64) loaded into registers and written into the
+//         other slot of a two-slot LDS ring at the end of the step (rows past
+//         M read as zero);
+//   codes of step k+2 loaded into registers (16 bytes per thread: eight
+//         threads per weight row);
 //   the MFMAs of step k run while the codes of step k+1 are decoded and
 //         written into the other W' buffer.
 // LDS: 2 x 32 KB (dY) + 2 x 36 KB (W', rows padded to 576 bytes so that a
@@ -477,29 +480,33 @@ __global__ __launch_bounds__(256, 1) void k_gemm_fwd(FwdTable tab, int64_t M, in
 // ---------------------------------------------------------------------------
 constexpr int kBwRow = 36;                     // 16-byte chunks per LDS row of the W' tile (32 + pad)
 constexpr int kBwChunks = 64 * kBwRow;
+constexpr int kBwThreads = 512;
 
 struct BCodes {
-  u32x4 p0, p1;    // the 32 code bytes of this thread's block
+  u32x4 p;         // this thread's 16 code bytes (half a 64-block)
   float d;
   int8_t q;
   float live;      // 1 for a real weight row, 0 past N
 };
 
 template <int RSN>
-__global__ __launch_bounds__(256, 1) void k_gemm_bwd(const uint16_t* __restrict__ dy, int64_t M, int64_t N,
-                                                     int64_t K, const uint8_t* __restrict__ packed,
-                                                     const int8_t* __restrict__ qscale,
-                                                     const float* __restrict__ step,
-                                                     const uint16_t* __restrict__ ul, int rp,
-                                                     const uint16_t* __restrict__ Al, int r, float scale,
-                                                     uint16_t* __restrict__ dx, Codebook cb) {
+__global__ __launch_bounds__(kBwThreads, 1) void k_gemm_bwd(const uint16_t* __restrict__ dy, int64_t M, int64_t N,
+                                                            int64_t K, const uint8_t* __restrict__ packed,
+                                                            const int8_t* __restrict__ qscale,
+                                                            const float* __restrict__ step,
+                                                            const uint16_t* __restrict__ ul, int rp,
+                                                            const uint16_t* __restrict__ Al, int r, float scale,
+                                                            uint16_t* __restrict__ dx, Codebook cb) {
+  // the two W' buffers are one array: after the main loop it holds A^T for
+  // the LoRA epilogue (up to 256 x 136 bf16)
   __shared__ u32x4 As0[kChunks];
   __shared__ u32x4 As1[kChunks];
-  __shared__ u32x4 Ws0[kBwChunks];
-  __shared__ u32x4 Ws1[kBwChunks];
+  __shared__ u32x4 Ws[2 * kBwChunks];
+  u32x4* const Ws0 = Ws;
+  u32x4* const Ws1 = Ws + kBwChunks;
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w >> 2, wn = w & 3;
   const int h = lane >> 5, l32 = lane & 31;
   const int ntm = static_cast<int>(cdiv(M, kTile)), ntk = static_cast<int>(cdiv(K, kTile));
   int tm, tk;
@@ -513,7 +520,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd(const uint16_t* __restrict_
   // dY tile staging through registers (not LDS DMA: the transposed LDS reads
   // of W' carry no alias information, so any LDS DMA in flight would make the
   // compiler wait for it before each of them). Thread t moves 16-byte chunk
-  // t & 7 of rows (t >> 3) + 32 i: eight lanes cover a row's 128 bytes.
+  // t & 7 of rows (t >> 3) + 64 i: eight lanes cover a row's 128 bytes.
   // Buffer loads through a descriptor over this tile's dY rows: rows past M
   // read as zero without a branch. (Columns past N in the last step read the
   // next row; the matching weight rows are dead, so they contribute zero.)
@@ -521,29 +528,28 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd(const uint16_t* __restrict_
   const int64_t rows_valid = imin(static_cast<int64_t>(kTile), M - m0);
   const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(dy + m0 * N), 0, static_cast<int>(rows_valid * N * 2), kBufferDword3);
-  uint32_t aoff[8];
+  uint32_t aoff[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) aoff[i] = static_cast<uint32_t>((arow0 + 32 * i) * N * 2 + 16 * ach);
-  u32x4 areg[8];
+  for (int i = 0; i < 4; ++i) aoff[i] = static_cast<uint32_t>((arow0 + 64 * i) * N * 2 + 16 * ach);
+  u32x4 areg[4];
   auto load_a = [&](int64_t st) {
     const uint32_t so = static_cast<uint32_t>(imin(st, nsteps - 1) * 128);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
       areg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(yr, aoff[i], so, 0));
   };
   auto store_a = [&](u32x4* Ab) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) Ab[a_slot(arow0 + 32 * i, ach)] = areg[i];
+    for (int i = 0; i < 4; ++i) Ab[a_slot(arow0 + 64 * i, ach)] = areg[i];
   };
-  // this thread decodes weight row (t >> 2) of the step, 64-column block t & 3
-  const int brow = t >> 2, bkb = t & 3;
+  // this thread decodes half bh = t >> 8 (columns 32 bh .. 32 bh + 31) of
+  // 64-column block t & 3 of weight row (t >> 2) & 63 of the step
+  const int brow = (t >> 2) & 63, bkb = t & 3, bh = t >> 8;
   const int64_t bkbi = imin(k0 / 64 + bkb, nbr - 1);
   auto load_codes = [&](int64_t st, BCodes& P) {
     const int64_t n = st * 64 + brow;
     const int64_t nc = imin(n, N - 1);
-    const uint8_t* pp = packed + nc * (K / 2) + bkbi * 32;
-    P.p0 = ld16(pp);
-    P.p1 = ld16(pp + 16);
+    P.p = ld16(packed + nc * (K / 2) + bkbi * 32 + 16 * bh);
     const int64_t blk = nc * nbr + bkbi;
     P.q = qscale[blk];
     P.d = step[blk >> 8];
@@ -555,11 +561,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd(const uint16_t* __restrict_
   // and a transposed read phase (4 rows x 4 aligned chunks of one block) still does.
   auto w_slot = [](int row, int c) { return row * kBwRow + (c ^ ((c >> 3) & 3)); };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
@@ -568,10 +574,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd(const uint16_t* __restrict_
   // 16-column half (G & 1) of the wave's 32-column block j
   const int G = lane >> 4, j16 = lane & 15;
   const int hh = G >> 1, cbh = G & 1;
-  auto read_b = [&](const u32x4* Wb, int s, bf16x8 (&bf)[4]) {
+  auto read_b = [&](const u32x4* Wb, int s, bf16x8 (&bf)[2]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = 128 * wn + 32 * j + 16 * cbh + 4 * (j16 & 3);
+    for (int j = 0; j < 2; ++j) {
+      const int col = 64 * wn + 32 * j + 16 * cbh + 4 * (j16 & 3);
       s16x4 v[2];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
@@ -596,17 +602,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd(const uint16_t* __restrict_
     load_codes(st + 2, ld);
     __builtin_amdgcn_sched_barrier(0);
     const MagTable tb = make_table(cb, block_scale(nx.q, nx.d) * nx.live);
-    const uint32_t pw[8] = {nx.p0.x, nx.p0.y, nx.p0.z, nx.p0.w, nx.p1.x, nx.p1.y, nx.p1.z, nx.p1.w};
-    bf16x8 af[2][4], bf[2][4];
+    const uint32_t pw[4] = {nx.p.x, nx.p.y, nx.p.z, nx.p.w};
+    bf16x8 af[2][4], bf[2][2];
     read_a(Ab, 0, af[0]);
     read_b(Wb, 0, bf[0]);
     __builtin_amdgcn_sched_barrier(0);
     // Each sub-step is its own scheduling region, issued in this order: its
     // first MFMA (operands read during the previous sub-step), then per MFMA
-    // one fragment read of the next sub-step and three VALU ops of the
-    // decode, then its W' writes (and in the last one the dY writes). Left
-    // free, the scheduler pulls MFMAs of later sub-steps forward, and those
-    // then wait for reads issued only just before.
+    // one fragment read of the next sub-step and a share of the decode, then
+    // its W' write (and in the last one the dY writes).
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (s < 3) {
@@ -616,20 +620,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd(const uint16_t* __restrict_
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(af[s & 1][i], bf[s & 1][j], acc[i][j]);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) Wn[w_slot(brow, 8 * bkb + 2 * s + c)] = decode8(pw[2 * s + c], tb);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[s & 1][i], bf[s & 1][j], acc[i][j]);
+      Wn[w_slot(brow, 8 * bkb + 4 * bh + s)] = decode8(pw[s], tb);
       if (s == 3) store_a(An);
 #pragma unroll
-      for (int m = 0; m < 16; ++m) {
+      for (int m = 0; m < 8; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (s < 3 && m < 12) __builtin_amdgcn_sched_group_barrier(0x080, 1, 0);
+        if (s < 3) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
       }
       if (s == 3)
-        __builtin_amdgcn_sched_group_barrier(0x200, 10, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 5, 0);
       else
-        __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -643,12 +646,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd(const uint16_t* __restrict_
   load_codes(1, P1);
   __builtin_amdgcn_sched_barrier(0);
   store_a(As0);
-  asm volatile("" ::"v"(P1.p0), "v"(P1.p1), "v"(static_cast<int>(P1.q)), "v"(P1.d));
+  asm volatile("" ::"v"(P1.p), "v"(static_cast<int>(P1.q)), "v"(P1.d));
   {
     const MagTable tb = make_table(cb, block_scale(P0.q, P0.d) * P0.live);
-    const uint32_t pw[8] = {P0.p0.x, P0.p0.y, P0.p0.z, P0.p0.w, P0.p1.x, P0.p1.y, P0.p1.z, P0.p1.w};
+    const uint32_t pw[4] = {P0.p.x, P0.p.y, P0.p.z, P0.p.w};
 #pragma unroll
-    for (int c = 0; c < 8; ++c) Ws0[w_slot(brow, 8 * bkb + c)] = decode8(pw[c], tb);
+    for (int c = 0; c < 4; ++c) Ws0[w_slot(brow, 8 * bkb + 4 * bh + c)] = decode8(pw[c], tb);
   }
   __syncthreads();
   // The end of step st waits for this wave's LDS writes (W' and dY of step
@@ -666,27 +669,28 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd(const uint16_t* __restrict_
 
   if constexpr (RSN > 0) {
     // The up-projection needs A transposed (ranks along the contraction): the
-    // r x 256 block of A under this tile goes through the LDS, free after the
-    // main loop, as At[col][rank] with rows of rp + 8 elements (16-byte
-    // aligned; the pad spreads a read phase over more banks). Ranks past r
-    // and columns past K are zero.
+    // r x 256 block of A under this tile goes through the W' buffers, free
+    // after the main loop, as At[col][rank] with rows of rp + 8 elements
+    // (16-byte aligned; the pad spreads a read phase over more banks). Ranks
+    // past r and columns past K are zero.
+    static_assert(256 * (128 + 8) * 2 <= 2 * kBwChunks * 16, "A^T does not fit the W' buffers");
     __syncthreads();
-    uint16_t* At = reinterpret_cast<uint16_t*>(As0);
+    uint16_t* At = reinterpret_cast<uint16_t*>(Ws);
     const int atw = rp + 8;
     {
       // 16 RSN rows x 32 chunks of 8 columns: every load issued before any
       // LDS write (K % 64 == 0, so a chunk is wholly inside or past K)
-      constexpr int kPer = 16 * RSN * 32 / 256;
+      constexpr int kPer = 16 * RSN * 32 / kBwThreads;
       u32x4 av[kPer];
 #pragma unroll
       for (int u = 0; u < kPer; ++u) {
-        const int e = t + 256 * u, j = e >> 5, c8 = (e & 31) * 8;
+        const int e = t + kBwThreads * u, j = e >> 5, c8 = (e & 31) * 8;
         const int64_t kc = k0 + c8;
         av[u] = (j < r && kc < K) ? ld16(Al + static_cast<int64_t>(j) * K + kc) : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int u = 0; u < kPer; ++u) {
-        const int e = t + 256 * u, j = e >> 5, c8 = (e & 31) * 8;
+        const int e = t + kBwThreads * u, j = e >> 5, c8 = (e & 31) * 8;
         const uint32_t wv[4] = {av[u].x, av[u].y, av[u].z, av[u].w};
 #pragma unroll
         for (int q = 0; q < 8; ++q)
@@ -694,48 +698,47 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd(const uint16_t* __restrict_
       }
     }
     __syncthreads();
+    // groups of IG row blocks: their u fragments are loaded before their
+    // MFMAs; the At fragments of one column block at a time
     auto lora = [&](auto rsn_c) {
       constexpr int RS = decltype(rsn_c)::value;
-      constexpr int JG = RS <= 2 ? 4 : 2;             // column blocks per group (registers)
-      u32x4 uf[4][RS];
+      constexpr int IG = RS <= 2 ? 4 : RS <= 4 ? 2 : 1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t mrow = imin(m0 + 128 * wm + 32 * i + l32, M - 1);
+      for (int i0 = 0; i0 < 4; i0 += IG) {
+        u32x4 uf[IG][RS];
 #pragma unroll
-        for (int rs = 0; rs < RS; ++rs) uf[i][rs] = ld16(ul + mrow * rp + 16 * rs + 8 * h);
-      }
+        for (int ii = 0; ii < IG; ++ii) {
+          const int64_t mrow = imin(m0 + 128 * wm + 32 * (i0 + ii) + l32, M - 1);
 #pragma unroll
-      for (int j0 = 0; j0 < 4; j0 += JG) {
-        u32x4 af[JG][RS];
-#pragma unroll
-        for (int jj = 0; jj < JG; ++jj) {
-          const int col = 128 * wn + 32 * (j0 + jj) + l32;
-#pragma unroll
-          for (int rs = 0; rs < RS; ++rs)
-            af[jj][rs] = *reinterpret_cast<const u32x4*>(At + col * atw + 16 * rs + 8 * h);
+          for (int rs = 0; rs < RS; ++rs) uf[ii][rs] = ld16(ul + mrow * rp + 16 * rs + 8 * h);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 2; ++j) {
+          const int col = 64 * wn + 32 * j + l32;
+          u32x4 af[RS];
 #pragma unroll
-          for (int jj = 0; jj < JG; ++jj) {
+          for (int rs = 0; rs < RS; ++rs) af[rs] = *reinterpret_cast<const u32x4*>(At + col * atw + 16 * rs + 8 * h);
+#pragma unroll
+          for (int ii = 0; ii < IG; ++ii) {
             f32x16 tmp;
 #pragma unroll
             for (int v = 0; v < 16; ++v) tmp[v] = 0.f;
 #pragma unroll
-            for (int rs = 0; rs < RS; ++rs) tmp = mfma32(as_bf16x8(uf[i][rs]), as_bf16x8(af[jj][rs]), tmp);
+            for (int rs = 0; rs < RS; ++rs) tmp = mfma32(as_bf16x8(uf[ii][rs]), as_bf16x8(af[rs]), tmp);
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j0 + jj][v] += scale * tmp[v];
+            for (int v = 0; v < 16; ++v) acc[i0 + ii][j][v] += scale * tmp[v];
           }
+        }
       }
     };
     lora(std::integral_constant<int, RSN>{});
   }
   if (m0 + kTile <= M && k0 + kTile <= K) {
-    uint16_t* dt = dx + (m0 + 128 * wm + 4 * h) * K + k0 + 128 * wn + l32;
+    uint16_t* dt = dx + (m0 + 128 * wm + 4 * h) * K + k0 + 64 * wn + l32;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v)
           dt[(32 * i + 8 * (v >> 2) + (v & 3)) * K + 32 * j] = bf16_bits(acc[i][j][v]);
@@ -743,8 +746,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_bwd(const uint16_t* __restrict_
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t kk = k0 + 128 * wn + 32 * j + l32;
+      for (int j = 0; j < 2; ++j) {
+        const int64_t kk = k0 + 64 * wn + 32 * j + l32;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int64_t mm = m0 + 128 * wm + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
@@ -881,7 +884,8 @@ hipError_t launch_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K, co
   }
   const int64_t tiles = cdiv(M, kTile) * cdiv(K, kTile);
 #define QNF4_BWD(RSNV)                                                                                         \
-  hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_bwd<RSNV>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, \
+  hipLaunchKernelGGL(HIP_KERNEL_NAME(k_gemm_bwd<RSNV>), dim3(static_cast<unsigned>(tiles)), dim3(kBwThreads), 0, \
+                     stream,                                                                                  \
                      dy, M, N, K, packed, qscale, step, static_cast<const uint16_t*>(lora), rp, A, r, scale, dx, cb)
   mark_kernel(0, stream);
   switch (rp / 16) {
