@@ -489,6 +489,7 @@ struct BCodes {
   float live;      // 1 for a real weight row, 0 past N
 };
 
+// RSN: rank chunks of 16 in the LoRA epilogue (1 for r <= 16, else rank_pad(r) / 16), 0 for none.
 template <int RSN>
 __global__ __launch_bounds__(kBwThreads, 1) void k_gemm_bwd(const uint16_t* __restrict__ dy, int64_t M, int64_t N,
                                                             int64_t K, const uint8_t* __restrict__ packed,
@@ -497,8 +498,8 @@ __global__ __launch_bounds__(kBwThreads, 1) void k_gemm_bwd(const uint16_t* __re
                                                             const uint16_t* __restrict__ ul, int rp,
                                                             const uint16_t* __restrict__ Al, int r, float scale,
                                                             uint16_t* __restrict__ dx, Codebook cb) {
-  // the two W' buffers are one array: after the main loop it holds A^T for
-  // the LoRA epilogue (up to 256 x 136 bf16)
+  // the two W' buffers are one array: after the main loop it holds A's
+  // slice for the LoRA epilogue (up to 128 ranks x 256 columns)
   __shared__ u32x4 As0[kChunks];
   __shared__ u32x4 As1[kChunks];
   __shared__ u32x4 Ws[2 * kBwChunks];
@@ -574,18 +575,19 @@ __global__ __launch_bounds__(kBwThreads, 1) void k_gemm_bwd(const uint16_t* __re
   // 16-column half (G & 1) of the wave's 32-column block j
   const int G = lane >> 4, j16 = lane & 15;
   const int hh = G >> 1, cbh = G & 1;
+  auto read_bj = [&](const u32x4* Wb, int s, int j) {
+    const int col = 64 * wn + 32 * j + 16 * cbh + 4 * (j16 & 3);
+    s16x4 v[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int row = 16 * s + 8 * hh + 4 * q + (j16 >> 2);
+      v[q] = ds_read_tr(Wb, w_slot(row, col >> 3) * 8 + (col & 4));
+    }
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  };
   auto read_b = [&](const u32x4* Wb, int s, bf16x8 (&bf)[2]) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = 64 * wn + 32 * j + 16 * cbh + 4 * (j16 & 3);
-      s16x4 v[2];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int row = 16 * s + 8 * hh + 4 * q + (j16 >> 2);
-        v[q] = ds_read_tr(Wb, w_slot(row, col >> 3) * 8 + (col & 4));
-      }
-      bf[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
-    }
+    for (int j = 0; j < 2; ++j) bf[j] = read_bj(Wb, s, j);
   };
   auto read_a = [&](const u32x4* Ab, int s, bf16x8 (&af)[4]) {
     const int sw = (2 * s + h) ^ a_swz(l32);       // a_swz(128 wm + 32 i + l32) == a_swz(l32)
@@ -668,38 +670,35 @@ __global__ __launch_bounds__(kBwThreads, 1) void k_gemm_bwd(const uint16_t* __re
   wait_vm<0>();
 
   if constexpr (RSN > 0) {
-    // The up-projection needs A transposed (ranks along the contraction): the
-    // r x 256 block of A under this tile goes through the W' buffers, free
-    // after the main loop, as At[col][rank] with rows of rp + 8 elements
-    // (16-byte aligned; the pad spreads a read phase over more banks). Ranks
-    // past r and columns past K are zero.
-    static_assert(256 * (128 + 8) * 2 <= 2 * kBwChunks * 16, "A^T does not fit the W' buffers");
+    // The up-projection contracts over the ranks: its B operand is the r x 256
+    // slice of A under this tile, staged row-major in the W' buffers (free
+    // after the main loop; the same padded, swizzled rows) and read with the
+    // main loop's transposed reads, rank chunk rs in place of sub-step s.
+    // Ranks past r and columns past K are zero. RSN counts the rank chunks
+    // of 16 that are used (1 for r <= 16: u's padding columns 16 .. 31 are
+    // zero and skipped).
+    static_assert(16 * 8 * kBwRow <= 2 * kBwChunks, "A's slice does not fit the W' buffers");
     __syncthreads();
-    uint16_t* At = reinterpret_cast<uint16_t*>(Ws);
-    const int atw = rp + 8;
     {
-      // 16 RSN rows x 32 chunks of 8 columns: every load issued before any
-      // LDS write (K % 64 == 0, so a chunk is wholly inside or past K)
+      // 16 RSN rows x 32 chunks of 8 columns (K % 64 == 0, so a chunk is
+      // wholly inside or past K), all loads before the LDS writes
       constexpr int kPer = 16 * RSN * 32 / kBwThreads;
       u32x4 av[kPer];
 #pragma unroll
       for (int u = 0; u < kPer; ++u) {
-        const int e = t + kBwThreads * u, j = e >> 5, c8 = (e & 31) * 8;
-        const int64_t kc = k0 + c8;
+        const int e = t + kBwThreads * u, j = e >> 5, ch = e & 31;
+        const int64_t kc = k0 + 8 * ch;
         av[u] = (j < r && kc < K) ? ld16(Al + static_cast<int64_t>(j) * K + kc) : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int u = 0; u < kPer; ++u) {
-        const int e = t + kBwThreads * u, j = e >> 5, c8 = (e & 31) * 8;
-        const uint32_t wv[4] = {av[u].x, av[u].y, av[u].z, av[u].w};
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          At[(c8 + q) * atw + j] = static_cast<uint16_t>(wv[q >> 1] >> (16 * (q & 1)));
+        const int e = t + kBwThreads * u;
+        Ws[w_slot(e >> 5, e & 31)] = av[u];
       }
     }
     __syncthreads();
     // groups of IG row blocks: their u fragments are loaded before their
-    // MFMAs; the At fragments of one column block at a time
+    // MFMAs; A's fragments read per column block
     auto lora = [&](auto rsn_c) {
       constexpr int RS = decltype(rsn_c)::value;
       constexpr int IG = RS <= 2 ? 4 : RS <= 4 ? 2 : 1;
@@ -714,17 +713,16 @@ __global__ __launch_bounds__(kBwThreads, 1) void k_gemm_bwd(const uint16_t* __re
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int col = 64 * wn + 32 * j + l32;
-          u32x4 af[RS];
+          bf16x8 bl[RS];
 #pragma unroll
-          for (int rs = 0; rs < RS; ++rs) af[rs] = *reinterpret_cast<const u32x4*>(At + col * atw + 16 * rs + 8 * h);
+          for (int rs = 0; rs < RS; ++rs) bl[rs] = read_bj(Ws, rs, j);
 #pragma unroll
           for (int ii = 0; ii < IG; ++ii) {
             f32x16 tmp;
 #pragma unroll
             for (int v = 0; v < 16; ++v) tmp[v] = 0.f;
 #pragma unroll
-            for (int rs = 0; rs < RS; ++rs) tmp = mfma32(as_bf16x8(uf[ii][rs]), as_bf16x8(af[rs]), tmp);
+            for (int rs = 0; rs < RS; ++rs) tmp = mfma32(as_bf16x8(uf[ii][rs]), bl[rs], tmp);
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i0 + ii][j][v] += scale * tmp[v];
           }
@@ -888,8 +886,9 @@ hipError_t launch_bwd_dx(const uint16_t* dy, int64_t M, int64_t N, int64_t K, co
                      stream,                                                                                  \
                      dy, M, N, K, packed, qscale, step, static_cast<const uint16_t*>(lora), rp, A, r, scale, dx, cb)
   mark_kernel(0, stream);
-  switch (rp / 16) {
+  switch (r == 0 ? 0 : r <= 16 ? 1 : rp / 16) {
     case 0: QNF4_BWD(0); break;
+    case 1: QNF4_BWD(1); break;
     case 2: QNF4_BWD(2); break;
     case 4: QNF4_BWD(4); break;
     case 6: QNF4_BWD(6); break;

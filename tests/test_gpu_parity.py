@@ -238,6 +238,8 @@ BWD_CASES = [
     (16, 4096, 64, 16, 32.0, 31),      # one block column, the rows split across workgroups
     (40, 200, 128, 32, 16.0, 32),      # B read in place, two rank tiles, a partial last chunk of N
     (33, 72, 64, 128, 8.0, 33),        # B read in place, eight rank tiles
+    (40, 136, 512, 128, 8.0, 34),      # tiled: A^T of the largest rank over two full column tiles
+    (300, 200, 320, 96, 16.0, 35),     # tiled: six rank tiles, ragged M and K
 ]
 
 
