@@ -102,7 +102,8 @@ struct BScale4 {   // the same for the four steps of a super-step
 // super-step are one aligned 4-byte word of qscale and share one second-level
 // step (a 256-block group never splits 4-aligned blocks); scales are then
 // loaded once per super-step. Otherwise they are loaded per step.
-// RSN: rank_pad(r) / 16 (chunks of 16 ranks in the LoRA epilogue), 0 for none.
+// RSN: chunks of 16 ranks in the LoRA epilogue (1 for r <= 16: t's padding
+// columns 16 .. 31 are zero and skipped; else rank_pad(r) / 16), 0 for none.
 template <bool kQuad, int RSN>
 __global__ __launch_bounds__(256, 1) void k_gemm_fwd(FwdTable tab, int64_t M, int rp, int r, float scale,
                                                      Codebook cb) {
@@ -807,8 +808,9 @@ static hipError_t launch_fwd_tiled(int64_t M, int G, const uint16_t* const* x, c
                          dim3(256), 0, stream, tab, M, rp, r, scale, cb);                                      \
   } while (0)
   mark_kernel(0, stream);
-  switch (rp / 16) {
+  switch (r == 0 ? 0 : r <= 16 ? 1 : rp / 16) {
     case 0: QNF4_FWD(0); break;
+    case 1: QNF4_FWD(1); break;
     case 2: QNF4_FWD(2); break;
     case 4: QNF4_FWD(4); break;
     case 6: QNF4_FWD(6); break;
