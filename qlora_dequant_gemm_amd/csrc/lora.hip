@@ -140,7 +140,9 @@ __global__ __launch_bounds__(64 * kDownWaves) void k_down_rows(const uint16_t* i
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int g = lane >> 4, c = lane & 15;
   const int m0 = blockIdx.x * 16;
-  const int rows_valid = M - m0 < 0 ? 0 : (M - m0 < 16 ? M - m0 : 16);
+  // uniform by construction; readfirstlane keeps the descriptors in scalar
+  // registers (otherwise every load through them becomes a per-lane loop)
+  const int rows_valid = __builtin_amdgcn_readfirstlane(M - m0 < 0 ? 0 : (M - m0 < 16 ? M - m0 : 16));
   u32x4* const mine = lds + w * kPer;
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(in + static_cast<int64_t>(m0) * Kc), 0, rows_valid * Kc * 2, kBufWord3);
@@ -155,37 +157,56 @@ __global__ __launch_bounds__(64 * kDownWaves) void k_down_rows(const uint16_t* i
 #pragma unroll
   for (int jt = 0; jt < RT; ++jt) acc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  // GS chunks per round, all their loads issued before their MFMAs
-  for (int q0 = w; q0 < nchunk; q0 += kDownWaves * GS) {
-    u32x4 xa[GS][2], wa[GS][RT][2];
-    u32x4 bl[kBT ? GS : 1][kBT ? 2 * RT : 1];
+  // GS chunks per round, all their loads issued before their MFMAs; two
+  // rounds in registers, the next one's loads issued before the current one's
+  // MFMAs, so each wave keeps a round of loads in flight while it computes
+  struct Round {
+    u32x4 xa[GS][2];
+    u32x4 wv[GS][2 * RT];      // kBT: the B-row pieces; else A rows 16 jt + c, pieces 0 / 1 at 2 jt / 2 jt + 1
+  };
+  // Loads are issued unconditionally (a conditional round would make the
+  // compiler's wait counts assume it missing and drain the pipeline): chunks
+  // past the end get an out-of-range offset, which reads zero without a
+  // memory access.
+  auto load_round = [&](int q0, Round& R) {
 #pragma unroll
     for (int u = 0; u < GS; ++u) {
-      const int q = q0 + kDownWaves * u < nchunk ? q0 + kDownWaves * u : nchunk - 1;
-      const uint32_t so = static_cast<uint32_t>(q * 128);
-      xa[u][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xo, so, 0));
-      xa[u][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xo + 16, so, 0));
+      const int qq = q0 + kDownWaves * u;
+      const bool dead = qq >= nchunk;
+      const int q = dead ? 0 : qq;
+      // wave-uniform; readfirstlane keeps it in a scalar register (a vector
+      // soffset turns every load into a per-lane loop)
+      const uint32_t so = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(q * 128));
+      const uint32_t off_dead = 0x80000000u;
+      const uint32_t xv = dead ? off_dead : xo;
+      R.xa[u][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xv, so, 0));
+      R.xa[u][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xv + 16, so, 0));
       if constexpr (kBT) {
         // B rows 64 q .. 64 q + 63: 16-byte piece lane + 64 e of the run
-        const uint32_t bo = static_cast<uint32_t>(q * 2048 * RT);
+        const uint32_t bo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(q * 2048 * RT));
 #pragma unroll
         for (int e = 0; e < 2 * RT; ++e)
-          bl[u][e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, 16 * (lane + 64 * e), bo, 0));
+          R.wv[u][e] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, dead ? off_dead : 16 * (lane + 64 * e), bo, 0));
       } else {
 #pragma unroll
         for (int jt = 0; jt < RT; ++jt) {
-          wa[u][jt][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, wo[jt], so, 0));
-          wa[u][jt][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, wo[jt] + 16, so, 0));
+          const uint32_t wv = dead ? off_dead : wo[jt];
+          R.wv[u][2 * jt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, wv, so, 0));
+          R.wv[u][2 * jt + 1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, wv + 16, so, 0));
         }
       }
     }
+  };
+  auto compute_round = [&](int q0, const Round& R) {
+    u32x4 wa[GS][RT][2];
     if constexpr (kBT) {
 #pragma unroll
       for (int u = 0; u < GS; ++u)
 #pragma unroll
         for (int e = 0; e < 2 * RT; ++e) {
-          const int pc = lane + 64 * e, sl = pc >> 1, R = sl / RT;
-          mine[u * 128 * RT + 2 * (sl ^ bt_swz<RT>(R)) + (pc & 1)] = bl[u][e];
+          const int pc = lane + 64 * e, sl = pc >> 1, Rw = sl / RT;
+          mine[u * 128 * RT + 2 * (sl ^ bt_swz<RT>(Rw)) + (pc & 1)] = R.wv[u][e];
         }
 #pragma unroll
       for (int u = 0; u < GS; ++u)
@@ -194,11 +215,19 @@ __global__ __launch_bounds__(64 * kDownWaves) void k_down_rows(const uint16_t* i
           s16x4 v[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int R = 16 * g + 4 * i + (c >> 2);
-            v[i] = ds_read_tr(mine + u * 128 * RT, 16 * ((R * RT + jt) ^ bt_swz<RT>(R)) + 4 * (c & 3));
+            const int Rw = 16 * g + 4 * i + (c >> 2);
+            v[i] = ds_read_tr(mine + u * 128 * RT, 16 * ((Rw * RT + jt) ^ bt_swz<RT>(Rw)) + 4 * (c & 3));
           }
           wa[u][jt][0] = __builtin_bit_cast(u32x4, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
           wa[u][jt][1] = __builtin_bit_cast(u32x4, __builtin_shufflevector(v[2], v[3], 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    } else {
+#pragma unroll
+      for (int u = 0; u < GS; ++u)
+#pragma unroll
+        for (int jt = 0; jt < RT; ++jt) {
+          wa[u][jt][0] = R.wv[u][2 * jt];
+          wa[u][jt][1] = R.wv[u][2 * jt + 1];
         }
     }
 #pragma unroll
@@ -207,12 +236,38 @@ __global__ __launch_bounds__(64 * kDownWaves) void k_down_rows(const uint16_t* i
       const int k = q * 64 + 16 * g;
       // a repeated last chunk, or pieces past Kc, contribute nothing
       const bool live0 = q < nchunk && k < Kc, live1 = q < nchunk && k + 8 < Kc;
-      const u32x4 x0 = live0 ? xa[u][0] : zero, x1 = live1 ? xa[u][1] : zero;
+      const u32x4 x0 = live0 ? R.xa[u][0] : zero, x1 = live1 ? R.xa[u][1] : zero;
 #pragma unroll
       for (int jt = 0; jt < RT; ++jt) {
         acc[jt] = mfma16(as_bf16x8(x0), as_bf16x8(live0 ? wa[u][jt][0] : zero), acc[jt]);
         acc[jt] = mfma16(as_bf16x8(x1), as_bf16x8(live1 ? wa[u][jt][1] : zero), acc[jt]);
       }
+    }
+  };
+  constexpr int kStep = kDownWaves * GS;       // chunks between a wave's rounds
+  // two rounds in registers where they fit (RT GS <= 4), else one at a time
+  constexpr bool kTwo = RT * GS <= 4;
+  Round R0;
+  if constexpr (kTwo) {
+    Round R1;
+    load_round(w, R0);
+    // the scheduling barriers keep each round's loads ahead of the MFMAs of
+    // the round before it
+    for (int q0 = w; q0 < nchunk; q0 += 2 * kStep) {
+      const int q1 = q0 + kStep;
+      __builtin_amdgcn_sched_barrier(0);
+      load_round(q1, R1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_round(q0, R0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_round(q1 + kStep, R0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_round(q1, R1);
+    }
+  } else {
+    for (int q0 = w; q0 < nchunk; q0 += kStep) {
+      load_round(q0, R0);
+      compute_round(q0, R0);
     }
   }
   // the wave's own region takes its partial sums (its last reads of the
@@ -303,9 +358,9 @@ hipError_t launch_lora_down(bool wrow, const uint16_t* in, int64_t M, int64_t Kc
     if (nt == 1)
       QNF4_DR(1, 4);
     else if (nt == 2)
-      QNF4_DR(2, 4);
+      QNF4_DR(2, 2);
     else if (nt == 4)
-      QNF4_DR(4, 2);
+      QNF4_DR(4, 1);
     else
       QNF4_DR(8, 1);
 #undef QNF4_DR

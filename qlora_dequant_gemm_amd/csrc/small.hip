@@ -59,6 +59,10 @@ namespace qnf4 {
 
 constexpr int kDbWaves = 4;
 constexpr int kDbBufWord3 = 0x00020000;        // raw buffer descriptor word 3 on gfx9-family parts
+// A wave-uniform value moved to a scalar register: buffer descriptors built
+// from it stay scalar (a descriptor the compiler holds in vector registers
+// turns every load through it into a per-lane loop).
+__device__ __forceinline__ int sgpr(int v) { return __builtin_amdgcn_readfirstlane(v); }
 constexpr int kDnCols = 64;                    // narrow items: dX columns (one block column)
 constexpr int kDnSub = 64;                     //   weight rows per sub-tile
 constexpr int kDnUChunks = 192;                //   16-byte chunks of one rank tile's B rows (padded)
@@ -453,7 +457,7 @@ __global__ __launch_bounds__(64 * kDbWaves, 2) void k_dec_bwd_wide(DecBwdBatch b
   // logical chunk ci % 32); for one rank tile they are loaded now, during the
   // main loop's first loads, and used after it
   const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(NTU > 0 ? P.A : P.dy), 0, NTU > 0 ? r * K * 2 : 0, kDbBufWord3);
+      const_cast<uint16_t*>(NTU > 0 ? P.A : P.dy), 0, sgpr(NTU > 0 ? r * K * 2 : 0), kDbBufWord3);
   auto load_a = [&](int jt, int hh) {
     const int ci = 256 * hh + t, j = 16 * jt + (ci >> 5), kk = k0 + 8 * (ci & 31);
     const uint32_t ao = (j < r && kk < K) ? static_cast<uint32_t>((j * K + kk) * 2) : 0x80000000u;
@@ -482,13 +486,13 @@ __global__ __launch_bounds__(64 * kDbWaves, 2) void k_dec_bwd_wide(DecBwdBatch b
     const int n0 = ss * kDwSS;
     if (w < 2) {
       const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t*>(P.dy + n0), 0, M * N * 2 - n0 * 2, kDbBufWord3);
+          const_cast<uint16_t*>(P.dy + n0), 0, sgpr(M * N * 2 - n0 * 2), kDbBufWord3);
 #pragma unroll
       for (int h = 0; h < 4; ++h)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(yr, (lds_void*)(ys + 256 * w + 64 * h), 16, doff[h], 0, 0, 0);
     } else if constexpr (kSB) {
       const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t*>(P.B + static_cast<int64_t>(n0) * 16), 0, (N - n0) * 32, kDbBufWord3);
+          const_cast<uint16_t*>(P.B + static_cast<int64_t>(n0) * 16), 0, sgpr((N - n0) * 32), kDbBufWord3);
 #pragma unroll
       for (int h = 0; h < 4; ++h)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void*)(bs + 256 * (w - 2) + 64 * h), 16, doff[h], 0, 0,
@@ -506,7 +510,7 @@ __global__ __launch_bounds__(64 * kDbWaves, 2) void k_dec_bwd_wide(DecBwdBatch b
   };
   constexpr bool kPreB = !kSB && NTU == 1;
   const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(NTU > 0 ? P.B : P.dy), 0, NTU > 0 ? N * r * 2 : 0, kDbBufWord3);
+      const_cast<uint16_t*>(NTU > 0 ? P.B : P.dy), 0, sgpr(NTU > 0 ? N * r * 2 : 0), kDbBufWord3);
   const int64_t ngroups = (static_cast<int64_t>(N) * nbr + 255) >> 8;
   // B[n][16 jt + 4g .. + 3] (zero past N or r)
   auto load_b = [&](int n, int jt) {
@@ -525,7 +529,7 @@ __global__ __launch_bounds__(64 * kDbWaves, 2) void k_dec_bwd_wide(DecBwdBatch b
     const int rows = N - nw0 < 0 ? 0 : (N - nw0 < 64 ? N - nw0 : 64);
     const int nb = rows > 0 ? nw0 : 0;
     const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(P.packed + static_cast<int64_t>(nb) * (K / 2)), 0, rows * (K / 2), kDbBufWord3);
+        const_cast<uint8_t*>(P.packed + static_cast<int64_t>(nb) * (K / 2)), 0, sgpr(rows * (K / 2)), kDbBufWord3);
 #pragma unroll
     for (int ch = 0; ch < 4; ++ch) {
       const uint32_t co = kvalid ? static_cast<uint32_t>((16 * ch + c) * (K / 2) + kb * 32) : 0x80000000u;
@@ -535,10 +539,10 @@ __global__ __launch_bounds__(64 * kDbWaves, 2) void k_dec_bwd_wide(DecBwdBatch b
     if constexpr (!kQuad) {
       const int64_t sb = static_cast<int64_t>(nb) * nbr;
       const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<int8_t*>(P.qscale + sb), 0, rows * nbr, kDbBufWord3);
+          const_cast<int8_t*>(P.qscale + sb), 0, sgpr(rows * nbr), kDbBufWord3);
       const int64_t g0 = sb >> 8;
       const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<float*>(P.step + g0), 0, static_cast<int>((ngroups - g0) * 4), kDbBufWord3);
+          const_cast<float*>(P.step + g0), 0, sgpr(static_cast<int>((ngroups - g0) * 4)), kDbBufWord3);
 #pragma unroll
       for (int ch = 0; ch < 4; ++ch) {
         const int bl = (16 * ch + c) * nbr + kb;
@@ -768,7 +772,7 @@ __global__ __launch_bounds__(64 * kDbWaves, 2) void k_dec_bwd_wide(DecBwdBatch b
   const int Mp = (M + 3) & ~3;
   float* const part_cg = bt.part + (P.part0 + static_cast<int64_t>(cg) * P.S) * (kDwCols * Mp);
   const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
-      part_cg, 0, P.S * kDwCols * Mp * 4, kDbBufWord3);
+      part_cg, 0, sgpr(P.S * kDwCols * Mp * 4), kDbBufWord3);
   if (4 * g < M) {
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
