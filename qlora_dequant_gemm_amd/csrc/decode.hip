@@ -57,6 +57,7 @@ constexpr int kDecNT = 4;                         // 16-row MFMA tiles per wave
 constexpr int kDecBufWord3 = 0x00020000;          // raw buffer descriptor word 3 on gfx9-family parts
 constexpr int kDecRows = 16 * kDecNT * 4;         // weight rows per item (four waves)
 constexpr int64_t kDecMaxSps = 8;               // 256-deep super-steps per item at most
+constexpr int kDecEarlyBItems = 768;            // launches up to this many items request B early
 
 __device__ __forceinline__ int dec_item_of(int wg, int grid) {
   // grid is a multiple of 8: XCD (wg % 8) gets items [xcd * grid/8, ...)
@@ -242,6 +243,33 @@ __global__ __launch_bounds__(256, 2) void k_dec_fwd(DecFwdBatch bt, Codebook cb)
   }
 
 
+  // B rows of the LoRA up-projection for this lane's four weight rows. In
+  // launches of at most one round of workgroups (a single weight or a small
+  // group: the workgroup's one item is the whole of its time) and with
+  // 16-byte rows (r % 8 == 0) they are requested at the start of the last
+  // super-step, so their latency overlaps its decode instead of adding one
+  // more round trip after it; in larger launches other items cover that
+  // latency and the registers are better left to the main loop. Pieces past r
+  // read as zero (out-of-range offset); rows past N repeat the last row (their
+  // outputs are never written).
+  constexpr int kRSb = RT > 0 ? kRS : 1;
+  u32x4 bop[kDecNT][kRSb];
+  const bool early_b = RT > 0 && (r & 7) == 0 && bt.items <= kDecEarlyBItems;
+  const __amdgpu_buffer_rsrc_t bbr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(RT > 0 ? P.B : P.x), 0, RT > 0 ? N * r * 2 : 0, kDecBufWord3);
+  auto load_b_early = [&] {
+#pragma unroll
+    for (int nt = 0; nt < kDecNT; ++nt) {
+      const int n = nb0 + 16 * nt + c < N ? nb0 + 16 * nt + c : N - 1;
+#pragma unroll
+      for (int rs = 0; rs < kRSb; ++rs) {
+        const int col = 32 * rs + 8 * g;
+        const uint32_t off = col < r ? static_cast<uint32_t>((n * r + col) * 2) : 0x80000000u;
+        bop[nt][rs] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(bbr, off, 0, 0));
+      }
+    }
+  };
+
   // iteration i: (1) every wave is past its reads of the stage buffer about to
   // be refilled (barrier); (2) request the codes and the stage of the next
   // super-step; (3) wait until this wave's part of the current stage has
@@ -262,6 +290,10 @@ __global__ __launch_bounds__(256, 2) void k_dec_fwd(DecFwdBatch bt, Codebook cb)
       // outstanding, oldest first: [codes i, stage i] [codes i+1, stage i+1]
       if (ndma) wait_vm<2 * kDecNT + 4 + (kQuad ? 0 : 2 * kDecNT)>();
       else wait_vm<2 * kDecNT + (kQuad ? 0 : 2 * kDecNT)>();
+    } else if (RT > 0 && early_b) {
+      load_b_early();
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm<kDecNT * kRSb>();                  // codes and stage of this step, not B
     } else {
       wait_vm<0>();
     }
@@ -330,13 +362,14 @@ __global__ __launch_bounds__(256, 2) void k_dec_fwd(DecFwdBatch bt, Codebook cb)
     // rows padded against bank conflicts where the 64 rows still fit in the stage buffers
     constexpr int kLd = 16 * kRT + (kRT < 8 ? 4 : 0);
     static_assert(4 * 16 * kLd * 4 <= sizeof(u32x4) * 2 * kDecStageChunks, "t exchange exceeds the stage buffers");
-    u32x4 bop[kDecNT][kRS];
+    if (!early_b || nit == 0) {
 #pragma unroll
-    for (int nt = 0; nt < kDecNT; ++nt) {
-      const int64_t n = imin(nb0 + 16 * nt + c, N - 1);
+      for (int nt = 0; nt < kDecNT; ++nt) {
+        const int64_t n = imin(nb0 + 16 * nt + c, N - 1);
 #pragma unroll
-      for (int rs = 0; rs < kRS; ++rs)
-        bop[nt][rs] = load_row8(P.B + n * r, 32 * rs + 8 * g, r, (r & 7) == 0);
+        for (int rs = 0; rs < kRS; ++rs)
+          bop[nt][rs] = load_row8(P.B + n * r, 32 * rs + 8 * g, r, (r & 7) == 0);
+      }
     }
 #pragma unroll
     for (int jt = 0; jt < kRT; ++jt)

@@ -200,6 +200,9 @@ FWD_CASES = [
     (300, 520, 320, 8, 16.0, 15),      # 2 x 3 tiles, ragged in M and N
     (513, 256, 128, 64, 16.0, 16),
     (260, 1, 64, 0, 0.0, 17),          # N = 1, no adapter
+    (40, 136, 512, 128, 8.0, 18),      # tiled, largest rank: down-projection one round at a time
+    (300, 200, 320, 96, 16.0, 19),     # tiled, six rank tiles padded to eight, ragged M and K
+    (17, 64, 6144, 16, 32.0, 20),      # down-projection: three rounds per wave (the last pair half past the end)
 ]
 
 
@@ -240,6 +243,7 @@ BWD_CASES = [
     (33, 72, 64, 128, 8.0, 33),        # B read in place, eight rank tiles
     (40, 136, 512, 128, 8.0, 34),      # tiled: A^T of the largest rank over two full column tiles
     (300, 200, 320, 96, 16.0, 35),     # tiled: six rank tiles, ragged M and K
+    (17, 6144, 64, 16, 32.0, 36),      # B read in place over three rounds per wave
 ]
 
 
