@@ -203,6 +203,8 @@ FWD_CASES = [
     (40, 136, 512, 128, 8.0, 18),      # tiled, largest rank: down-projection one round at a time
     (300, 200, 320, 96, 16.0, 19),     # tiled, six rank tiles padded to eight, ragged M and K
     (17, 64, 6144, 16, 32.0, 20),      # down-projection: three rounds per wave (the last pair half past the end)
+    (4, 520, 512, 64, 16.0, 21),       # decode, four rank tiles, B rows requested during the last super-step
+    (5, 300, 320, 24, 8.0, 22),        # decode, rank 24: the last 8-rank piece of each B row past r
 ]
 
 
