@@ -722,9 +722,10 @@ CALL_KERNEL = {"quantize_dq": ("k_quantize", "quant.hip"), "fwd": ("k_dec_fwd", 
 
 def kernel_times(wl, stream, M, reps_max=32):
     """Per call label whose main kernel is a matmul: ms of that kernel alone,
-    from two HIP events the library records on the launch stream right
-    before and after it (qlora_set_kernel_events), averaged over the label's
-    calls issued one at a time."""
+    from HIP events the library records on the launch stream right before and
+    after it (qlora_set_kernel_events), averaged over the label's calls. The
+    calls are issued back to back, each with its own pair of events, so the
+    stream never waits for the host between an event and its kernel."""
     import ctypes
     import torch
     from qlora_dequant_gemm_amd import _lib
@@ -734,35 +735,39 @@ def kernel_times(wl, stream, M, reps_max=32):
     hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
     hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
     hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
-    e0, e1 = ctypes.c_void_p(), ctypes.c_void_p()
-    if hip.hipEventCreate(ctypes.byref(e0)) or hip.hipEventCreate(ctypes.byref(e1)):
-        raise RuntimeError("hipEventCreate failed")
+    ev = [(ctypes.c_void_p(), ctypes.c_void_p()) for _ in range(reps_max)]
+    made = []
     L = _lib.lib()
     out = {}
     try:
+        for e0, e1 in ev:
+            if hip.hipEventCreate(ctypes.byref(e0)) or hip.hipEventCreate(ctypes.byref(e1)):
+                raise RuntimeError("hipEventCreate failed")
+            made += [e0, e1]
         for lab, fns in wl.timing_groups():
             if kernel_of(lab, M)[0] == "k_quantize":
                 continue
             with torch.cuda.stream(stream):
                 fns[0]()
             torch.cuda.synchronize()
-            L.qlora_set_kernel_events(e0, e1)
-            tot, n = 0.0, 0
-            for fn in fns[:reps_max]:
-                with torch.cuda.stream(stream):
+            calls = fns[:reps_max]
+            with torch.cuda.stream(stream):
+                for fn, (e0, e1) in zip(calls, ev):
+                    L.qlora_set_kernel_events(e0, e1)
                     fn()
+            L.qlora_set_kernel_events(None, None)
+            tot = 0.0
+            for _, (e0, e1) in zip(calls, ev):
                 ms = ctypes.c_float()
                 if hip.hipEventSynchronize(e1) or hip.hipEventElapsedTime(ctypes.byref(ms), e0, e1):
                     raise RuntimeError(f"kernel events of {lab} not recorded")
                 tot += ms.value
-                n += 1
-            L.qlora_set_kernel_events(None, None)
-            out[lab] = tot / n
+            out[lab] = tot / len(calls)
     finally:
         L.qlora_set_kernel_events(None, None)
         torch.cuda.synchronize()
-        hip.hipEventDestroy(e0)
-        hip.hipEventDestroy(e1)
+        for e in made:
+            hip.hipEventDestroy(e)
     return out
 
 
